@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the chain hot path on one MI355X.
+
+One step = one causal GQA attention forward over the 65536-token workload
+(32 query heads over 8 key/value heads, head_dim 128, bf16, 16 zigzag KV
+chunks merged on chip), inputs resident in HBM before timing starts.  Prints
+one JSON line: TFLOP/s (causal FLOPs = 4*B*Hq*S*S*D/2), the roofline of the
+attention kernel, the float64 oracle timed on a bounded sample on the host,
+and secondary figures for the other workloads (4096-token MHA, the ring
+share with its log-sum-exp merge, the MLP chain).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
+       [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+HEADLINE = "attn_gqa_bf16_h32kv8_s65536_d128"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_flops(B, Hq, Sq, Sk, D, causal=True):
+    f = 4.0 * B * Hq * Sq * Sk * D
+    return f / 2 if causal else f
+
+
+def time_region(torch, fn, steps, warmup, stream):
+    """Mean ms per call of fn over `steps` calls, HIP events on `stream`."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def headline(torch, chain, steps, warmup):
+    from gemm_chain_amd.workloads import WORKLOADS, gen_attention
+    w = WORKLOADS[HEADLINE]
+    dev = torch.device("cuda:0")
+    log(f"generating inputs for {w.name}")
+    q, k, v = gen_attention(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.amp, w.seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        chain.attn_fwd(qd, kd, vd, causal=True, n_chunks=w.n_chunks, zigzag=w.zigzag, out=o, lse=lse)
+
+    log(f"timing {steps} steps after {warmup} warmup")
+    ms = time_region(torch, step, steps, warmup, stream)
+    flops = attn_flops(w.B, w.Hq, w.S, w.S, w.D)
+    return w, (q, k, v), ms, flops
+
+
+def cpu_baseline(w, inputs, budget_s=12.0):
+    """The float64 oracle on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    q, k, v = inputs
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    S = w.S
+    blocks = [int(x) for x in np.linspace(0, S - 256, 64)]
+    order = [blocks[i] for i in np.random.default_rng(0).permutation(len(blocks))]
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    for r0 in order:
+        rows = np.arange(r0, r0 + 256)
+        oracle.attention_rows(qn, kn, vn, 0, 0, rows, causal=True, scale=w.scale)
+        flops += 4.0 * w.D * float((rows + 1).sum())         # visible pairs of these rows
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} blocks of 256 query rows of head 0 (positions spread over the "
+                      f"{S}-token sequence), float64 numpy, {dt:.1f} s"}
+
+
+def secondary(torch, chain, steps):
+    """Other workloads: MHA 4096, ring share + merge, MLP chain."""
+    import numpy as np
+    from gemm_chain_amd.workloads import WORKLOADS, gen_attention, gen_mlp
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+
+    w = WORKLOADS["attn_bf16_b2_h32_s4096_d128"]
+    q, k, v = (t.to(dev) for t in gen_attention(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.amp, w.seed))
+    o = torch.empty_like(q)
+    l = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    ms = time_region(torch, lambda: chain.attn_fwd(q, k, v, causal=True, out=o, lse=l), steps, 2, stream)
+    tf = attn_flops(w.B, w.Hq, w.S, w.S, w.D) / ms / 1e9
+    out[w.name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, o, l
+
+    w = WORKLOADS["ring_share_bf16_h32_s32768_r0of8"]
+    q, k, v = gen_attention(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.amp, w.seed)
+    P, r = w.ring_ranks, w.ring_rank
+    qruns = chain.zigzag_segments(w.S, P, r)
+    qpos = np.concatenate([np.arange(a, a + n) for a, n in qruns])
+    ql = q[:, :, qpos].contiguous().to(dev)
+    chunks = []
+    for s in [(r - i) % P for i in range(P)]:
+        kruns = chain.zigzag_segments(w.S, P, s)
+        kpos = np.concatenate([np.arange(a, a + n) for a, n in kruns])
+        chunks.append((kruns, k[:, :, kpos].contiguous().to(dev), v[:, :, kpos].contiguous().to(dev)))
+    B, H, Sl, D = ql.shape
+    op = torch.empty((P, B, H, Sl, D), dtype=torch.float32, device=dev)
+    lp = torch.empty((P, B, H, Sl), dtype=torch.float32, device=dev)
+    om = torch.empty((B, H, Sl, D), dtype=torch.bfloat16, device=dev)
+    lm = torch.empty((B, H, Sl), dtype=torch.float32, device=dev)
+
+    def partials():
+        for i, (kruns, kc, vc) in enumerate(chunks):
+            chain.attn_partial(ql, kc, vc, qruns, kruns, causal=True, out=op[i], lse=lp[i])
+
+    def merge():
+        chain.lse_merge(op, lp, out=om, lse=lm)
+
+    ms_p = time_region(torch, partials, steps, 2, stream)
+    ms_m = time_region(torch, merge, steps * 4, 2, stream)
+    # visible pairs of the share: 2 P n^2 + n per head, n = S / 2P
+    n = w.S // (2 * P)
+    flops = 4.0 * B * H * D * (2 * P * n * n + n)
+    merge_bytes = P * B * H * Sl * (4 * D + 4) + B * H * Sl * (2 * D + 4)
+    out[w.name] = {"ms_partials": round(ms_p, 4), "ms_merge": round(ms_m, 4),
+                   "tflops_partials": round(flops / ms_p / 1e9, 1),
+                   "tflops_end_to_end": round(flops / (ms_p + ms_m) / 1e9, 1),
+                   "merge_gbs": round(merge_bytes / ms_m / 1e6, 1),
+                   "merge_frac_hbm": round(merge_bytes / ms_m / 1e6 / PEAK_HBM_GBS, 4)}
+    del chunks, ql, op, lp, om, lm
+
+    w = WORKLOADS["mlp_bf16_m16384_k4096_n1376"]
+    x, w1, w2 = (t.to(dev) for t in gen_mlp(w.M, w.K, w.N, dtype=w.dtype, amp_x=w.amp_x,
+                                            amp_w=w.amp_w, seed=w.seed))
+    o = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(chain.mlp_workspace_bytes(w.M, w.N), dtype=torch.uint8, device=dev)
+    ms = time_region(torch, lambda: chain.mlp_fwd(x, w1, w2, act=w.act, out=o, workspace=ws), steps, 2, stream)
+    flops = 4.0 * w.M * w.K * w.N
+    out[w.name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                   "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the sharded "
+              "design is described, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gemm_chain_amd import chain
+    chain.load()
+    w, inputs, ms, flops = headline(torch, chain, args.steps, args.warmup)
+    tflops = flops / ms / 1e9
+    log(f"{w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
+    record = {
+        "metric": "causal attention fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "seq_len": w.S, "head_dim": w.D, "causal": True, "kv_chunks": w.n_chunks,
+                   "zigzag": w.zigzag, "parallelism": "single GPU"},
+        "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        # one step is one launch of the attention kernel, so its mean duration is ms_per_step
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_secondary:
+        log("secondary workloads")
+        record["secondary"] = secondary(torch, chain, max(3, args.steps))
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        record["cpu_baseline"] = cpu_baseline(w, inputs)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

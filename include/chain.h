@@ -1,0 +1,222 @@
+/*
+ * libchain -- the two-matmul chain O = f(A.B).C on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (METP article, FITEE doi 10.1631/FITEE.2400602, abstract): the
+ * core unit of Transformer training is two consecutive matrix products with an
+ * optional function between them.  Two instances are provided:
+ *
+ *   attention  A = Q, B = K^T, C = V, f = row softmax of scale * scores under an
+ *              optional causal mask over global positions (TSP article, section
+ *              "Lo que realmente significa plegar": causal attention needs the
+ *              whole key/value context, which arrives reordered in zigzag
+ *              pieces); query heads may share key/value heads in contiguous
+ *              groups (2D-Attention summary, "Comprendiendo la Arquitectura de
+ *              los LLMs": GQA).  Every row also yields its log-sum-exp
+ *              LSE_i = log sum_j exp(s_ij), natural log, over visible keys j.
+ *   MLP        A = X, B = W1, C = W2, f = GeLU (exact erf form, tanh form, or
+ *              identity).
+ *
+ * Chunked evaluation and merging (2D-Attention summary, "Introduciendo la
+ * Atencion 2D": tensors are chunked along the context; TSP article: partial
+ * outputs are accumulated locally): attention over a union of disjoint key
+ * sets equals the log-sum-exp merge of the per-set results,
+ *   M = max_c LSE_c,  w_c = exp(LSE_c - M),  LSE = M + log sum w_c,
+ *   O = sum_c w_c O_c / sum_c w_c,
+ * with parts whose LSE is -inf ignored.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Memory: every tensor's data lives in device memory of the current HIP
+ *   device; the caller allocates and owns all of it (including the MLP
+ *   workspace).  The library never allocates or frees device memory and keeps
+ *   no state between calls other than a thread-local error message.
+ * - Layout: chain_tensor gives shape and strides in ELEMENTS; the last
+ *   dimension must be contiguous (stride 1), other strides are free (>= 0).
+ *   Attention tensors are [B, H, S, D]; LSE tensors are [B, H, S]; partial
+ *   tensors carry a leading chunk dimension [C, B, H, S, D] / [C, B, H, S].
+ * - Alignment: data pointers and every non-unit stride times the element size
+ *   must be multiples of 16 bytes (CHAIN_ERR_ALIGN otherwise).
+ * - Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *   only enqueue work on it and return at once; results are visible after the
+ *   caller synchronises the stream.  Calls are reentrant; concurrent calls on
+ *   different streams are independent.
+ * - Errors: arguments are validated synchronously before anything is
+ *   launched; a call that fails validation has no side effect and returns a
+ *   status other than CHAIN_OK, with details in chain_last_error().  A failed
+ *   launch returns CHAIN_ERR_HIP.  Device faults surface at the caller's next
+ *   synchronisation, as for any HIP work.
+ * - Aliasing: outputs must not overlap inputs (CHAIN_ERR_ALIAS).
+ * - Empty inputs: zero-sized batch, head or query dimensions are valid and
+ *   launch nothing.
+ */
+#ifndef CHAIN_H
+#define CHAIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CHAIN_VERSION 100           /* 1.0.0 */
+#define CHAIN_MAX_DIMS 5
+#define CHAIN_MAX_RUNS 4            /* position runs per chain_segs */
+#define CHAIN_MAX_CHUNKS 64         /* n_chunks limit of chain_attn_fwd */
+
+typedef enum {
+  CHAIN_OK = 0,
+  CHAIN_ERR_NULL = 1,         /* a required pointer is NULL */
+  CHAIN_ERR_DTYPE = 2,        /* unsupported or mismatched element type */
+  CHAIN_ERR_SHAPE = 3,        /* inconsistent shapes or chunk counts */
+  CHAIN_ERR_LAYOUT = 4,       /* last dimension not contiguous, negative stride */
+  CHAIN_ERR_ALIGN = 5,        /* pointer or stride not 16-byte aligned */
+  CHAIN_ERR_ALIAS = 6,        /* an output overlaps an input */
+  CHAIN_ERR_UNSUPPORTED = 7,  /* valid request outside what the kernels cover */
+  CHAIN_ERR_WORKSPACE = 8,    /* MLP workspace missing or too small */
+  CHAIN_ERR_HIP = 9           /* the HIP runtime reported an error */
+} chain_status;
+
+typedef enum { CHAIN_F32 = 0, CHAIN_BF16 = 1 } chain_dtype;
+
+typedef enum {
+  CHAIN_ACT_GELU_ERF = 0,     /* x * Phi(x) */
+  CHAIN_ACT_GELU_TANH = 1,    /* x/2 * (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+  CHAIN_ACT_IDENTITY = 2
+} chain_act;
+
+/* A strided view of device memory.  dtype is a chain_dtype. */
+typedef struct {
+  void *data;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[CHAIN_MAX_DIMS];
+  int64_t stride[CHAIN_MAX_DIMS];
+} chain_tensor;
+
+/* Global sequence positions of the rows of a tensor, as n runs of consecutive
+ * positions: row sum_{r'<r} len[r'] + t has position start[r] + t.  Runs must
+ * be in ascending order and must not overlap (start[r+1] >= start[r]+len[r]),
+ * so positions strictly increase with the row index.  Host memory. */
+typedef struct {
+  int32_t n;
+  int64_t start[CHAIN_MAX_RUNS];
+  int64_t len[CHAIN_MAX_RUNS];
+} chain_segs;
+
+/* Library version (CHAIN_VERSION of the build). */
+int chain_version(void);
+
+/* Static text naming a status. */
+const char *chain_status_str(chain_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *chain_last_error(void);
+
+/*
+ * chain_attn_fwd -- whole attention of Q against K/V, the key/value context
+ * visited chunk by chunk with an online softmax (running max and log-sum-exp)
+ * merge kept on chip, so O and LSE are final.
+ *
+ *   Q   [B, Hq, S, D]   f32 or bf16            (input)
+ *   K,V [B, Hkv, S, D]  same dtype as Q        (input), Hq % Hkv == 0,
+ *                       query head h uses key/value head h / (Hq / Hkv)
+ *   O   [B, Hq, S, D]   same dtype as Q        (output)
+ *   LSE [B, Hq, S]      f32, natural log       (output)
+ *   causal   nonzero: key j visible to query i iff j <= i
+ *   scale    multiplies Q.K^T (finite, usually 1/sqrt(D))
+ *   n_chunks 1..CHAIN_MAX_CHUNKS key chunks visited in order 0..n_chunks-1;
+ *            S must be a multiple of n_chunks (of 2*n_chunks with zigzag)
+ *   zigzag   nonzero: chunk s is the pieces s and 2*n_chunks-1-s of a split
+ *            of S into 2*n_chunks equal pieces (TSP article, zigzag partition);
+ *            zero: chunk s is the s-th of n_chunks contiguous ranges
+ * The result does not depend on n_chunks/zigzag beyond floating-point
+ * rounding.  D must be 64 or 128 (CHAIN_ERR_UNSUPPORTED otherwise).
+ */
+chain_status chain_attn_fwd(const chain_tensor *Q, const chain_tensor *K,
+                            const chain_tensor *V, const chain_tensor *O,
+                            const chain_tensor *LSE, int causal, float scale,
+                            int n_chunks, int zigzag, void *stream);
+
+/*
+ * chain_attn_partial -- one step of ring / zigzag sequence-parallel attention
+ * (TSP article, "Lo que realmente significa plegar"; 2D-Attention summary,
+ * "Introduciendo la Atencion 2D"): local queries attend to one arriving
+ * key/value chunk and produce a partial result for chain_lse_merge.
+ *
+ *   Q        [B, Hq, Sq, D]   f32 or bf16, rows at positions q_pos   (input)
+ *   Kc, Vc   [B, Hkv, Sk, D]  same dtype, rows at positions kv_pos   (input)
+ *   O_part   [B, Hq, Sq, D]   f32                                    (output)
+ *   LSE_part [B, Hq, Sq]      f32                                    (output)
+ *   q_pos, kv_pos  host chain_segs covering exactly Sq and Sk rows
+ * With causal, key j is visible to query i iff kv_pos(j) <= q_pos(i).  A row
+ * that sees no key gets O_part = 0 and LSE_part = -inf (never NaN).
+ * Sk == 0 is valid (every row is then such a row).  D must be 64 or 128.
+ */
+chain_status chain_attn_partial(const chain_tensor *Q, const chain_tensor *Kc,
+                                const chain_tensor *Vc, const chain_tensor *O_part,
+                                const chain_tensor *LSE_part, int causal, float scale,
+                                const chain_segs *q_pos, const chain_segs *kv_pos,
+                                void *stream);
+
+/*
+ * chain_lse_merge -- combine C partial results by log-sum-exp (formula above).
+ *
+ *   O_parts   [C, B, H, S, D]  f32   (input)
+ *   LSE_parts [C, B, H, S]     f32   (input)
+ *   O         [B, H, S, D]     f32 or bf16 (output, rounded to nearest even)
+ *   LSE       [B, H, S]        f32   (output; may be NULL to skip it)
+ * Rows whose parts are all -inf give O = 0, LSE = -inf.  1 <= C <= 64.
+ * D must be a multiple of 4 and at most 256.
+ */
+chain_status chain_lse_merge(const chain_tensor *O_parts, const chain_tensor *LSE_parts,
+                             const chain_tensor *O, const chain_tensor *LSE, void *stream);
+
+/*
+ * chain_mlp_fwd -- O = act(X.W1).W2 (METP article, abstract; TSP article: one
+ * weight shard of the MLP ring).
+ *
+ *   X  [M, K]   bf16 or f32 (input)      W1 [K, N]  same dtype (input)
+ *   W2 [N, K2]  same dtype (input)       O  [M, K2] bf16 or f32 (output)
+ *   workspace   device buffer of at least chain_mlp_workspace_bytes(M, N, dtype)
+ *               bytes, 256-byte aligned; holds H = act(X.W1) in the input dtype
+ *               (bf16 H is rounded to nearest even, as the second product's
+ *               MFMA operand).  Owned by the caller; contents are scratch.
+ * Accumulation is f32.  K, N, K2 must be multiples of 8.
+ */
+chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1,
+                           const chain_tensor *W2, const chain_tensor *O, int act,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace chain_mlp_fwd needs for an M x N intermediate of dtype
+ * dt (a chain_dtype), rounded up to 256.  0 for an invalid dtype. */
+size_t chain_mlp_workspace_bytes(int64_t M, int64_t N, int32_t dt);
+
+/*
+ * chain_zigzag_segs -- host helper: the positions of share r of `parts` in a
+ * zigzag split of S tokens (TSP article, zigzag partition): the pieces r and
+ * 2*parts-1-r of 2*parts equal pieces, as two runs in ascending order.  Used
+ * both for a rank's query share and for zigzag key/value chunks.
+ * S must be a positive multiple of 2*parts and 0 <= r < parts.
+ */
+chain_status chain_zigzag_segs(int64_t S, int32_t parts, int32_t r, chain_segs *out);
+
+/*
+ * chain_attn_tile_census -- host helper describing the causal tile schedule
+ * that chain_attn_fwd / chain_attn_partial apply: over query tiles of
+ * block_m rows and key tiles of block_n rows (tiles cut inside each run /
+ * chunk range as the kernels cut them), count tiles fully visible (`full`),
+ * partly visible (`diag`, masked element by element) and invisible (`skip`,
+ * never computed).  kv_pos NULL means positions 0..Sk-1; n_chunks/zigzag as
+ * in chain_attn_fwd (ignored when kv_pos is given).  Host only.
+ */
+chain_status chain_attn_tile_census(int64_t Sq, const chain_segs *q_pos, int64_t Sk,
+                                    const chain_segs *kv_pos, int n_chunks, int zigzag,
+                                    int causal, int block_m, int block_n,
+                                    int64_t *full, int64_t *diag, int64_t *skip);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHAIN_H */

@@ -1,0 +1,219 @@
+"""The C ABI without a GPU: exports, validation status codes, host schedule.
+
+Every call here either is a pure host helper or fails validation before any
+launch (descriptors carry fake, never-dereferenced device addresses), so no
+GPU work is attempted.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from gemm_chain_amd import chain
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "chain.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(chain_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(chain.library_path()):
+        pytest.skip("libchain.so not built")
+    return chain.load()
+
+
+def td(shape, dtype=chain.BF16, data=FAKE, stride=None):
+    t = chain.ChainTensor()
+    t.data = data
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if stride is None:
+        stride, acc = [], 1
+        for n in reversed(shape):
+            stride.insert(0, acc)
+            acc *= n
+    for i, (n, s) in enumerate(zip(shape, stride)):
+        t.shape[i] = n
+        t.stride[i] = s
+    return t
+
+
+def test_every_declared_function_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.chain_version() == 100
+    assert lib.chain_status_str(0) == b"CHAIN_OK"
+    assert lib.chain_status_str(6) == b"CHAIN_ERR_ALIAS"
+
+
+def _attn(lib, Q, K, V, O, L, causal=1, scale=0.125, n_chunks=1, zigzag=0):
+    P = ctypes.byref
+    return lib.chain_attn_fwd(P(Q), P(K), P(V), P(O), P(L), causal, scale, n_chunks, zigzag, None)
+
+
+def _valid(B=1, Hq=4, Hkv=2, S=256, D=64, dt=chain.BF16, odt=None):
+    es = 4 if dt == chain.F32 else 2
+    base = FAKE
+    sz = B * Hq * S * D * es
+    Q = td([B, Hq, S, D], dt, base)
+    K = td([B, Hkv, S, D], dt, base + 1 * 2 ** 30)
+    V = td([B, Hkv, S, D], dt, base + 2 * 2 ** 30)
+    O = td([B, Hq, S, D], dt if odt is None else odt, base + 3 * 2 ** 30)
+    L = td([B, Hq, S], chain.F32, base + 4 * 2 ** 30)
+    assert sz < 2 ** 30
+    return Q, K, V, O, L
+
+
+CODES = {n: i for i, n in enumerate(chain.STATUS)}
+
+
+def test_attn_validation_codes(lib):
+    Q, K, V, O, L = _valid()
+    P = ctypes.byref
+    assert lib.chain_attn_fwd(None, P(K), P(V), P(O), P(L), 1, 0.1, 1, 0, None) == CODES["CHAIN_ERR_NULL"]
+    Qn = _valid()[0]
+    Qn.data = None
+    assert _attn(lib, Qn, K, V, O, L) == CODES["CHAIN_ERR_NULL"]
+    Kf = _valid(dt=chain.F32)[1]
+    assert _attn(lib, Q, Kf, V, O, L) == CODES["CHAIN_ERR_DTYPE"]
+    Lb = td([1, 4, 256], chain.BF16, FAKE + 4 * 2 ** 30)
+    assert _attn(lib, Q, K, V, O, Lb) == CODES["CHAIN_ERR_DTYPE"]
+    Ob = _valid(odt=chain.F32)[3]
+    assert _attn(lib, Q, K, V, Ob, L) == CODES["CHAIN_ERR_DTYPE"]
+    K3 = td([1, 3, 256, 64], chain.BF16, FAKE + 2 ** 30)
+    V3 = td([1, 3, 256, 64], chain.BF16, FAKE + 2 * 2 ** 30)
+    assert _attn(lib, Q, K3, V3, O, L) == CODES["CHAIN_ERR_SHAPE"]            # 4 % 3
+    Os = td([1, 4, 255, 64], chain.BF16, FAKE + 3 * 2 ** 30)
+    assert _attn(lib, Q, K, V, Os, L) == CODES["CHAIN_ERR_SHAPE"]
+    Qs = td([1, 4, 256, 64], chain.BF16, FAKE, stride=[4 * 256 * 128, 256 * 128, 128, 2])
+    assert _attn(lib, Qs, K, V, O, L) == CODES["CHAIN_ERR_LAYOUT"]
+    Qa = td([1, 4, 256, 64], chain.BF16, FAKE + 8)
+    assert _attn(lib, Qa, K, V, O, L) == CODES["CHAIN_ERR_ALIGN"]
+    Qr = td([1, 4, 256, 64], chain.BF16, FAKE, stride=[4 * 256 * 68, 256 * 68, 68, 1])
+    assert _attn(lib, Qr, K, V, O, L) == CODES["CHAIN_ERR_ALIGN"]             # 136-byte rows
+    Oal = td([1, 4, 256, 64], chain.BF16, FAKE + 4096)                           # overlaps Q
+    assert _attn(lib, Q, K, V, Oal, L) == CODES["CHAIN_ERR_ALIAS"]
+    Q96, K96, V96, O96, L96 = _valid(D=96)
+    assert _attn(lib, Q96, K96, V96, O96, L96) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    assert _attn(lib, Q, K, V, O, L, scale=0.0) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    assert _attn(lib, Q, K, V, O, L, scale=float("nan")) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    assert _attn(lib, Q, K, V, O, L, n_chunks=3) == CODES["CHAIN_ERR_SHAPE"]      # 256 % 3
+    assert _attn(lib, Q, K, V, O, L, n_chunks=256, zigzag=1) == CODES["CHAIN_ERR_SHAPE"]
+    assert _attn(lib, Q, K, V, O, L, n_chunks=0) == CODES["CHAIN_ERR_SHAPE"]
+    assert _attn(lib, Q, K, V, O, L, n_chunks=65) == CODES["CHAIN_ERR_SHAPE"]
+    Kl, Vl = td([1, 2, 512, 64], chain.BF16, FAKE + 2 ** 30), td([1, 2, 512, 64], chain.BF16, FAKE + 2 * 2 ** 30)
+    assert _attn(lib, Q, Kl, Vl, O, L, causal=1) == CODES["CHAIN_ERR_SHAPE"]    # causal needs Sk == Sq
+    assert b"multiple" in lib.chain_last_error() or lib.chain_last_error() != b""
+
+
+def test_partial_validation_codes(lib):
+    Q, K, V, _, L = _valid()
+    O = td([1, 4, 256, 64], chain.F32, FAKE + 3 * 2 ** 30)
+    P = ctypes.byref
+    good = chain.segs([(0, 128), (1000, 128)])
+    assert lib.chain_attn_partial(P(Q), P(K), P(V), P(O), P(L), 1, 0.1, P(good), None, None) == CODES["CHAIN_ERR_NULL"]
+    short = chain.segs([(0, 100)])
+    assert lib.chain_attn_partial(P(Q), P(K), P(V), P(O), P(L), 1, 0.1, P(good), P(short), None) == CODES["CHAIN_ERR_SHAPE"]
+    overlapping = chain.segs([(0, 200), (100, 56)])
+    assert lib.chain_attn_partial(P(Q), P(K), P(V), P(O), P(L), 1, 0.1, P(overlapping), P(good), None) == CODES["CHAIN_ERR_SHAPE"]
+    Ob = td([1, 4, 256, 64], chain.BF16, FAKE + 3 * 2 ** 30)
+    assert lib.chain_attn_partial(P(Q), P(K), P(V), P(Ob), P(L), 1, 0.1, P(good), P(good), None) == CODES["CHAIN_ERR_DTYPE"]
+
+
+def test_merge_and_mlp_validation_codes(lib):
+    P = ctypes.byref
+    Op = td([8, 1, 4, 256, 64], chain.F32, FAKE)
+    Lp = td([8, 1, 4, 256], chain.F32, FAKE + 2 ** 30)
+    O = td([1, 4, 256, 64], chain.BF16, FAKE + 2 * 2 ** 30)
+    L = td([1, 4, 256], chain.F32, FAKE + 3 * 2 ** 30)
+    Lpb = td([8, 1, 4, 256], chain.BF16, FAKE + 2 ** 30)
+    assert lib.chain_lse_merge(P(Op), P(Lpb), P(O), P(L), None) == CODES["CHAIN_ERR_DTYPE"]
+    Lp7 = td([7, 1, 4, 256], chain.F32, FAKE + 2 ** 30)
+    assert lib.chain_lse_merge(P(Op), P(Lp7), P(O), P(L), None) == CODES["CHAIN_ERR_SHAPE"]
+    Oal = td([1, 4, 256, 64], chain.BF16, FAKE + 64)
+    assert lib.chain_lse_merge(P(Op), P(Lp), P(Oal), P(L), None) == CODES["CHAIN_ERR_ALIAS"]
+
+    X = td([512, 256], chain.BF16, FAKE)
+    W1 = td([256, 128], chain.BF16, FAKE + 2 ** 30)
+    W2 = td([128, 256], chain.BF16, FAKE + 2 * 2 ** 30)
+    Om = td([512, 256], chain.BF16, FAKE + 3 * 2 ** 30)
+    need = lib.chain_mlp_workspace_bytes(512, 128, chain.BF16)
+    assert need == 512 * 128 * 2
+    ws = FAKE + 4 * 2 ** 30
+    assert lib.chain_mlp_fwd(P(X), P(W1), P(W2), P(Om), 0, ws, need - 1, None) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert lib.chain_mlp_fwd(P(X), P(W1), P(W2), P(Om), 0, None, need, None) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert lib.chain_mlp_fwd(P(X), P(W1), P(W2), P(Om), 7, ws, need, None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    W1b = td([255, 128], chain.BF16, FAKE + 2 ** 30)
+    assert lib.chain_mlp_fwd(P(X), P(W1b), P(W2), P(Om), 0, ws, need, None) == CODES["CHAIN_ERR_SHAPE"]
+    W1f = td([256, 128], chain.F32, FAKE + 2 ** 30)
+    assert lib.chain_mlp_fwd(P(X), P(W1f), P(W2), P(Om), 0, ws, need, None) == CODES["CHAIN_ERR_DTYPE"]
+    assert lib.chain_mlp_fwd(P(X), P(W1), P(W2), P(Om), 0, FAKE + 256, need, None) == CODES["CHAIN_ERR_ALIAS"]
+
+
+@pytest.mark.parametrize("S,P", [(32, 1), (256, 8), (32768, 8), (96, 3)])
+def test_zigzag_segments_match_oracle(lib, S, P):
+    for r in range(P):
+        runs = chain.zigzag_segments(S, P, r)
+        pos = np.concatenate([np.arange(a, a + n) for a, n in runs])
+        assert np.array_equal(pos, oracle.zigzag_share_positions(S, P, r))
+    with pytest.raises(chain.ChainError):
+        chain.zigzag_segments(S + 1, P, 0)
+    with pytest.raises(chain.ChainError):
+        chain.zigzag_segments(S, P, P)
+
+
+def _census_from_mask(qpos, kranges, causal, bm, bn):
+    """Tile classes recomputed from the oracle's visibility mask."""
+    full = diag = skip = 0
+    for r0 in range(0, len(qpos), bm):
+        qp = qpos[r0:r0 + bm]
+        for kpos in kranges:
+            for k0 in range(0, len(kpos), bn):
+                kp = kpos[k0:k0 + bn]
+                vis = oracle.visible_mask(qp, kp, causal)
+                if not vis.any():
+                    skip += 1
+                elif vis.all() and len(kp) == bn:
+                    full += 1
+                else:
+                    diag += 1
+    return full, diag, skip
+
+
+@pytest.mark.parametrize("Sq,bm,bn,n_chunks,zigzag", [
+    (256, 32, 64, 1, False), (256, 32, 64, 4, True), (300, 32, 64, 1, False),
+    (512, 128, 64, 8, True), (1024, 32, 64, 16, True), (192, 32, 64, 3, False)])
+def test_tile_census_fused_matches_mask(lib, Sq, bm, bn, n_chunks, zigzag):
+    ranges = [oracle.zigzag_chunk_positions(Sq, n_chunks, s) if zigzag else
+              oracle.natural_chunk_positions(Sq, n_chunks, s) for s in range(n_chunks)]
+    if zigzag:  # the kernels cut tiles inside each piece of a zigzag chunk
+        n = Sq // (2 * n_chunks)
+        ranges = [piece for r in ranges for piece in (r[:n], r[n:])]
+    got = chain.tile_census(Sq, Sq, n_chunks=n_chunks, zigzag=zigzag, block_m=bm, block_n=bn)
+    assert got == _census_from_mask(np.arange(Sq), ranges, True, bm, bn)
+    # every visible pair is covered by a FULL or DIAG tile, none by a SKIP tile
+    assert got[0] + got[1] + got[2] == sum(-(-Sq // bm) * -(-len(r) // bn) for r in ranges)
+
+
+def test_tile_census_ring_share(lib):
+    S, P = 2048, 8
+    qruns = chain.zigzag_segments(S, P, 0)
+    qpos = oracle.zigzag_share_positions(S, P, 0)
+    for s in range(P):
+        kruns = chain.zigzag_segments(S, P, s)
+        kpos = oracle.zigzag_chunk_positions(S, P, s)
+        n = S // (2 * P)
+        got = chain.tile_census(len(qpos), len(kpos), q_pos=qruns, kv_pos=kruns, block_m=32, block_n=64)
+        assert got == _census_from_mask(qpos, [kpos[:n], kpos[n:]], True, 32, 64)

@@ -1,0 +1,66 @@
+"""GPU parity of chain_mlp_fwd (O = act(X.W1).W2) against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_chain_amd import chain
+from gemm_chain_amd.workloads import WORKLOADS, gen_mlp
+from gpu_util import TOL_BF16, TOL_F32, announce, device, f64, max_abs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M,K,N,K2,dtype,act", [
+    (300, 256, 136, 264, "bf16", "gelu_erf"),      # ragged M, N and K2 tiles
+    (257, 512, 1376, 512, "bf16", "gelu_tanh"),    # inner width of the FFN shard
+    (64, 128, 64, 128, "bf16", "identity"),
+    (200, 136, 72, 96, "f32", "gelu_erf"),         # f32 MFMA path
+])
+def test_mlp_small_full_compare(M, K, N, K2, dtype, act):
+    dev = device()
+    x, w1, w2 = gen_mlp(M, K, N, K2, dtype=dtype, amp_x=1.0, amp_w=0.05, seed=40 + M)
+    announce(f"mlp M{M} K{K} N{N} K2{K2} {dtype} {act}")
+    o = chain.mlp_fwd(x.to(dev), w1.to(dev), w2.to(dev), act=act)
+    torch.cuda.synchronize()
+    ref = oracle.mlp(f64(x), f64(w1), f64(w2), act)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    err = max_abs(f64(o), ref)
+    print(f"max-abs {err:.3e}")
+    assert err <= tol
+
+
+def test_mlp_ffn_shard_m16384_sampled():
+    w = WORKLOADS["mlp_bf16_m16384_k4096_n1376"]
+    dev = device()
+    x, w1, w2 = gen_mlp(w.M, w.K, w.N, dtype=w.dtype, amp_x=w.amp_x, amp_w=w.amp_w, seed=w.seed)
+    announce("mlp 16384x4096x1376 full size")
+    o = chain.mlp_fwd(x.to(dev), w1.to(dev), w2.to(dev), act=w.act)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.M, 160, w.seed, extra=(127, 128, 8191))
+    ref = oracle.mlp(f64(x[rows]), f64(w1), f64(w2), w.act)
+    err = max_abs(f64(o.cpu()[rows]), ref)
+    print(f"max-abs {err:.3e} over {len(rows)} rows")
+    assert err <= TOL_BF16
+
+
+def test_mlp_shard_sum_equals_whole():
+    """Summing the outputs of inner-dimension shards gives the unsharded chain."""
+    dev = device()
+    x, w1, w2 = gen_mlp(256, 256, 512, 256, dtype="f32", amp_x=1.0, amp_w=0.05, seed=50)
+    xd, w1d, w2d = x.to(dev), w1.to(dev), w2.to(dev)
+    announce("mlp shard sum")
+    whole = chain.mlp_fwd(xd, w1d, w2d, act="gelu_erf")
+    parts = sum(chain.mlp_fwd(xd, w1d[:, s:s + 128].contiguous(), w2d[s:s + 128].contiguous(),
+                              act="gelu_erf") for s in range(0, 512, 128))
+    assert (whole - parts).abs().max().item() <= 1e-4
+
+
+def test_mlp_zero_input():
+    dev = device()
+    _, w1, w2 = gen_mlp(8, 64, 64, 64, seed=51)
+    x = torch.zeros(128, 64, dtype=torch.bfloat16, device=dev)
+    announce("mlp X = 0")
+    o = chain.mlp_fwd(x, w1.to(dev), w2.to(dev))
+    assert torch.all(o == 0)
