@@ -29,6 +29,25 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 HEADLINE = "attn_gqa_bf16_h32kv8_s65536_d128"
 
 
+def committed_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, if it was taken on the current kernel source (else None)."""
+    import hashlib
+    import re
+    summary = os.path.join(ROOT, "profiles", "attn_gqa_s65536_d128_hbm_counters.md")
+    src = os.path.join(ROOT, "gemm_chain_amd", "csrc", "attn_mfma.hip")
+    try:
+        text = open(summary).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    if t and h and h.group(1) == digest:
+        return int(t.group(1))
+    return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -172,6 +191,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run a plain device copy of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the sharded "
@@ -204,8 +225,16 @@ def main():
         # one step is one launch of the attention kernel, so its mean duration is ms_per_step
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": committed_traffic()},
     }
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        record["copy_calibration_bytes"] = args.copy_calibration
+        del src, dst
     if not args.no_secondary:
         log("secondary workloads")
         record["secondary"] = secondary(torch, chain, max(3, args.steps))

@@ -63,8 +63,11 @@ int64_t numel(const chain_tensor &t) {
   return n;
 }
 
-// Structural checks common to every tensor argument.
-chain_status check_tensor(const chain_tensor *t, const char *name, int ndim) {
+// Structural checks common to every tensor argument.  `align` is the byte
+// alignment the kernels need for the data pointer and every outer stride
+// (16 where rows are moved as 16-byte vectors, the element size where a
+// tensor is accessed element by element).
+chain_status check_tensor(const chain_tensor *t, const char *name, int ndim, int align = 16) {
   if (t == nullptr) return fail(CHAIN_ERR_NULL, "%s: descriptor is NULL", name);
   if (t->ndim != ndim) return fail(CHAIN_ERR_SHAPE, "%s: expected %d dims, got %d", name, ndim, t->ndim);
   if (elem_size(t->dtype) == 0) return fail(CHAIN_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
@@ -78,11 +81,11 @@ chain_status check_tensor(const chain_tensor *t, const char *name, int ndim) {
     return fail(CHAIN_ERR_LAYOUT, "%s: last dimension must be contiguous (stride %lld)", name,
                 (long long)t->stride[ndim - 1]);
   const size_t es = elem_size(t->dtype);
-  if (((uintptr_t)t->data) % 16)
-    return fail(CHAIN_ERR_ALIGN, "%s: data pointer not 16-byte aligned", name);
+  if (((uintptr_t)t->data) % align)
+    return fail(CHAIN_ERR_ALIGN, "%s: data pointer not %d-byte aligned", name, align);
   for (int i = 0; i < ndim - 1; ++i)
-    if (t->shape[i] > 1 && (t->stride[i] * (int64_t)es) % 16)
-      return fail(CHAIN_ERR_ALIGN, "%s: stride[%d] * %zu bytes not a multiple of 16", name, i, es);
+    if (t->shape[i] > 1 && (t->stride[i] * (int64_t)es) % align)
+      return fail(CHAIN_ERR_ALIGN, "%s: stride[%d] * %zu bytes not a multiple of %d", name, i, es, align);
   return CHAIN_OK;
 }
 
@@ -120,7 +123,7 @@ chain_status check_attn(const chain_tensor *Q, const chain_tensor *K, const chai
   TRY(check_tensor(K, partial ? "Kc" : "K", 4));
   TRY(check_tensor(V, partial ? "Vc" : "V", 4));
   TRY(check_tensor(O, partial ? "O_part" : "O", 4));
-  TRY(check_tensor(L, partial ? "LSE_part" : "LSE", 3));
+  TRY(check_tensor(L, partial ? "LSE_part" : "LSE", 3, 4));
   if (K->dtype != Q->dtype || V->dtype != Q->dtype)
     return fail(CHAIN_ERR_DTYPE, "Q, K and V must share one dtype");
   if (partial ? O->dtype != CHAIN_F32 : O->dtype != Q->dtype)
@@ -239,9 +242,9 @@ chain_status chain_attn_partial(const chain_tensor *Q, const chain_tensor *Kc, c
 chain_status chain_lse_merge(const chain_tensor *O_parts, const chain_tensor *LSE_parts,
                              const chain_tensor *O, const chain_tensor *LSE, void *stream) {
   TRY(check_tensor(O_parts, "O_parts", 5));
-  TRY(check_tensor(LSE_parts, "LSE_parts", 4));
-  TRY(check_tensor(O, "O", 4));
-  if (LSE) TRY(check_tensor(LSE, "LSE", 3));
+  TRY(check_tensor(LSE_parts, "LSE_parts", 4, 4));
+  TRY(check_tensor(O, "O", 4, O && O->dtype == CHAIN_F32 ? 16 : 8));
+  if (LSE) TRY(check_tensor(LSE, "LSE", 3, 4));
   if (O_parts->dtype != CHAIN_F32 || LSE_parts->dtype != CHAIN_F32)
     return fail(CHAIN_ERR_DTYPE, "partials must be f32");
   if (LSE && LSE->dtype != CHAIN_F32) return fail(CHAIN_ERR_DTYPE, "LSE must be f32");
@@ -296,7 +299,7 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
   TRY(check_tensor(X, "X", 2));
   TRY(check_tensor(W1, "W1", 2));
   TRY(check_tensor(W2, "W2", 2));
-  TRY(check_tensor(O, "O", 2));
+  TRY(check_tensor(O, "O", 2, O && O->dtype == CHAIN_F32 ? 4 : 2));
   if (W1->dtype != X->dtype || W2->dtype != X->dtype)
     return fail(CHAIN_ERR_DTYPE, "X, W1 and W2 must share one dtype");
   if (act != CHAIN_ACT_GELU_ERF && act != CHAIN_ACT_GELU_TANH && act != CHAIN_ACT_IDENTITY)

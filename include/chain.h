@@ -34,8 +34,11 @@
  *   dimension must be contiguous (stride 1), other strides are free (>= 0).
  *   Attention tensors are [B, H, S, D]; LSE tensors are [B, H, S]; partial
  *   tensors carry a leading chunk dimension [C, B, H, S, D] / [C, B, H, S].
- * - Alignment: data pointers and every non-unit stride times the element size
- *   must be multiples of 16 bytes (CHAIN_ERR_ALIGN otherwise).
+ * - Alignment (CHAIN_ERR_ALIGN otherwise): for tensors whose rows the kernels
+ *   move as 16-byte vectors (Q, K, V, attention O, O_parts, X, W1, W2) the
+ *   data pointer and every outer stride times the element size must be
+ *   multiples of 16 bytes; 8 bytes for a bf16 merge output; LSE tensors and
+ *   the MLP output only need element alignment.
  * - Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
  *   only enqueue work on it and return at once; results are visible after the
  *   caller synchronises the stream.  Calls are reentrant; concurrent calls on
