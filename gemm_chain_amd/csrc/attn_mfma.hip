@@ -28,7 +28,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BN = 64;  // keys per tile
+constexpr int BN = 64;          // keys per tile
+constexpr float kTau = 8.0f;    // lazy rescale threshold (base-2 exponent)
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -58,7 +59,8 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
   constexpr int ROWS = 32 * WQ;             // query positions per tile
   constexpr int KS = D / 16;                // k-steps of K.Q^T
   constexpr int DB = D / 32;                // 32-wide blocks of O^T
-  constexpr int LDK = D + 8, LDV = D + 8;   // padded LDS row pitch (elements)
+  constexpr int LDK = D + 8;                // K pitch: conflict-free 16-byte reads
+  constexpr int LDV = D + 16;               // V pitch: conflict-free transposing reads
   constexpr int CPR = D / 8;                // 16-byte chunks per key row
   constexpr int LOADS = BN * CPR / (NW * 64);
   constexpr int BUF = BN * (LDK + LDV);
@@ -189,13 +191,16 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
           }
         }
         if (cls == TILE_DIAG) {
+          // key of register r in lane half h2 is kb*32 + 8*(r/4) + 4*h2 + r%4: compare
+          // its compile-time part with per-lane limits (branch-free selects)
+          const int lim_c = p.causal ? my_qpos - k0 - off - 4 * h2 : BN;
+          const int lim = min(nvalid - 1 - 4 * h2, lim_c);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int key = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-              const bool vis = key < nvalid && (!p.causal || k0 + key + off <= my_qpos);
-              if (!vis) s[kb][r] = -INFINITY;
+              const int kr = kb * 32 + 8 * (r >> 2) + (r & 3);
+              s[kb][r] = kr <= lim ? s[kb][r] : -INFINITY;
             }
         }
         float mx = -INFINITY;
@@ -203,10 +208,18 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m, mx * c);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        // the reference max is raised only when the row max exceeds it by more
+        // than 2^kTau (exact: O and l share the reference); the O rescale is rare
+        const float tmax = pair_max(mx) * c;
+        if (__any(tmax > m + kTau)) {
+          const float m_new = fmaxf(m, tmax);
+          const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+          m = m_new;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        }
+        const float m_use = m == -INFINITY ? 0.f : m;
         float rs = 0.f;
         bf16x8 pk[2][2];
 #pragma unroll
@@ -217,10 +230,7 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
             rs += e;
             pk[kb][r >> 3][r & 7] = (__bf16)e;
           }
-        l = l * alpha + rs;
-        m = m_new;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        l += rs;
         // O^T += V^T . P^T
         const int trow = 4 * h2 + ((lane & 15) >> 2);
         const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
