@@ -4,20 +4,29 @@
 // scaled, masked row softmax, over key/value ranges visited chunk by chunk (the
 // zigzag chunks of the TSP article, "Lo que realmente significa plegar"; the
 // context chunks of the 2D-Attention summary, "Introduciendo la Atencion 2D"),
-// merging chunks with an online softmax that carries the running max m and sum
-// l in registers.  GQA (2D-Attention summary, "Comprendiendo la Arquitectura de
-// los LLMs"): the waves of one workgroup take query heads of the same key/value
-// head so a staged key/value tile serves all of them.
+// merging chunks with an online softmax that carries a reference max m and the
+// sum l in registers.  GQA (2D-Attention summary, "Comprendiendo la
+// Arquitectura de los LLMs"): the waves of one workgroup take query heads of
+// the same key/value head, so a staged key/value tile serves all of them.
 //
 // Per wave: 32 query rows of one head.  S^T = K.Q^T with v_mfma_f32_32x32x16_bf16
 // (keys are the M index, queries the N index), so each lane owns one query
-// column and 16 key rows per 32-key block: row max and row sum are in-lane
-// reductions plus one exchange between lane halves (v_permlane32_swap).  The
-// S^T accumulator, rounded to bf16, is directly the B operand of
-// O^T += V^T.P^T: within each 16-key step lane half h holds keys
-// {4h..4h+3, 8+4h..8+4h+3}, and the V^T operand is read in that order from the
-// row-major V tile with ds_read_b64_tr_b16.  K/V tiles are double-buffered in
-// LDS (global loads for tile i+1 are in flight while tile i is computed).
+// column and 16 key rows per 32-key block: the row max is an in-lane reduction
+// plus one exchange between lane halves (v_permlane32_swap), the row sum stays
+// per lane until the epilogue.  The S^T accumulator, rounded to bf16, is
+// directly the B operand of O^T += V^T.P^T: within each 16-key step lane half h
+// holds keys {4h..4h+3, 8+4h..8+4h+3}, and the V^T operand is read in that
+// order from the row-major V tile with ds_read_b64_tr_b16.
+//
+// Eight waves per workgroup (two per SIMD) share each staged 64-key K/V tile;
+// tiles are double-buffered in LDS with the global loads of tile i+1 in flight
+// while tile i is computed.  LDS pitches are chosen for conflict-free 16-byte
+// K reads (D+8) and conflict-free transposing V reads (D+32).  Inside each MFMA
+// run the LDS fragments are read kAhead MFMAs ahead of use (pinned with
+// scheduling barriers) and the wave raises its issue priority, so the other
+// wave on the SIMD fills the VALU (softmax) while this one feeds the matrix
+// core.  The reference max is raised only when a row's max grows past it by
+// more than 2^8 (exact: O and l share the reference), so the O rescale is rare.
 #include "internal.h"
 
 namespace chain {
@@ -30,6 +39,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 64;          // keys per tile
 constexpr float kTau = 8.0f;    // lazy rescale threshold (base-2 exponent)
+constexpr int kAhead = 4;       // LDS fragments in flight ahead of their MFMA
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -60,7 +70,7 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
   constexpr int KS = D / 16;                // k-steps of K.Q^T
   constexpr int DB = D / 32;                // 32-wide blocks of O^T
   constexpr int LDK = D + 8;                // K pitch: conflict-free 16-byte reads
-  constexpr int LDV = D + 16;               // V pitch: conflict-free transposing reads
+  constexpr int LDV = D + 32;               // V pitch: conflict-free transposing reads
   constexpr int CPR = D / 8;                // 16-byte chunks per key row
   constexpr int LOADS = BN * CPR / (NW * 64);
   constexpr int BUF = BN * (LDK + LDV);
@@ -182,14 +192,23 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
         const __bf16 *ks = smem + buf * BUF;
         const __bf16 *vs = ks + BN * LDK;
         f32x16 s[2] = {f32x16{}, f32x16{}};
+        __builtin_amdgcn_s_setprio(1);
+        {
+          constexpr int N = 2 * KS;
+          auto addr = [&](int i) { return ks + ((i & 1) * 32 + l32) * LDK + (i >> 1) * 16 + 8 * h2; };
+          bf16x8 kf[kAhead];
 #pragma unroll
-        for (int kstep = 0; kstep < KS; ++kstep) {
+          for (int i = 0; i < kAhead; ++i) kf[i] = *(const bf16x8 *)addr(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 a = *(const bf16x8 *)(ks + (kb * 32 + l32) * LDK + kstep * 16 + 8 * h2);
-            s[kb] = mfma32(a, qf[kstep], s[kb]);
+          for (int i = 0; i < N; ++i) {
+            const bf16x8 a = kf[i % kAhead];
+            if (i + kAhead < N) kf[i % kAhead] = *(const bf16x8 *)addr(i + kAhead);
+            s[i & 1] = mfma32(a, qf[i >> 1], s[i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (cls == TILE_DIAG) {
           // key of register r in lane half h2 is kb*32 + 8*(r/4) + 4*h2 + r%4: compare
           // its compile-time part with per-lane limits (branch-free selects)
@@ -234,19 +253,32 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
         // O^T += V^T . P^T
         const int trow = 4 * h2 + ((lane & 15) >> 2);
         const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        __builtin_amdgcn_s_setprio(1);
+        {
+          constexpr int N = 4 * DB;
+          auto addr = [&](int i) {
+            const int db = i >> 2, kb = (i >> 1) & 1, hh = i & 1;
+            return vs + (kb * 32 + 16 * hh + trow) * LDV + db * 32 + tcol;
+          };
+          i16x4 vlo[kAhead], vhi[kAhead];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int i = 0; i < kAhead; ++i) {
+            vlo[i] = ds_read_tr(addr(i));
+            vhi[i] = ds_read_tr(addr(i) + 8 * LDV);
+          }
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const __bf16 *src = vs + (kb * 32 + 16 * hh + trow) * LDV + db * 32 + tcol;
-              const i16x4 lo = ds_read_tr(src);
-              const i16x4 hi = ds_read_tr(src + 8 * LDV);
-              const i16x8 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-              acc[db] = mfma32(__builtin_bit_cast(bf16x8, a16), pk[kb][hh], acc[db]);
+          for (int i = 0; i < N; ++i) {
+            const i16x8 a16 = __builtin_shufflevector(vlo[i % kAhead], vhi[i % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
+            if (i + kAhead < N) {
+              vlo[i % kAhead] = ds_read_tr(addr(i + kAhead));
+              vhi[i % kAhead] = ds_read_tr(addr(i + kAhead) + 8 * LDV);
             }
+            acc[i >> 2] = mfma32(__builtin_bit_cast(bf16x8, a16), pk[(i >> 1) & 1][i & 1], acc[i >> 2]);
+        __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (more) swrite(buf ^ 1);
       __syncthreads();
       buf ^= 1;
@@ -294,9 +326,9 @@ hipError_t launch(const AttnParams &p, hipStream_t s) {
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const int group = p.Hq / p.Hkv;
-  if (group % 4 == 0) return launch<D, 4, 4>(p, s);
-  if (group % 2 == 0) return launch<D, 4, 2>(p, s);
-  return launch<D, 4, 1>(p, s);
+  if (group % 4 == 0) return launch<D, 8, 4>(p, s);
+  if (group % 2 == 0) return launch<D, 8, 2>(p, s);
+  return launch<D, 8, 1>(p, s);
 }
 
 }  // namespace
