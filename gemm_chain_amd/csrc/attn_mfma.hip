@@ -19,14 +19,17 @@
 // order from the row-major V tile with ds_read_b64_tr_b16.
 //
 // Eight waves per workgroup (two per SIMD) share each staged 64-key K/V tile;
-// tiles are double-buffered in LDS with the global loads of tile i+1 in flight
-// while tile i is computed.  LDS pitches are chosen for conflict-free 16-byte
+// tiles are double-buffered in LDS, and the global loads run two tiles ahead
+// (two register sets: tile i+2 is fetched while tile i is computed and tile
+// i+1, fetched one step earlier, is written to the free LDS buffer).  LDS pitches are chosen for conflict-free 16-byte
 // K reads (D+8) and conflict-free transposing V reads (D+32).  Inside each MFMA
 // run the LDS fragments are read kAhead MFMAs ahead of use (pinned with
 // scheduling barriers) and the wave raises its issue priority, so the other
 // wave on the SIMD fills the VALU (softmax) while this one feeds the matrix
 // core.  The reference max is raised only when a row's max grows past it by
 // more than 2^8 (exact: O and l share the reference), so the O rescale is rare.
+// The row sum l adds the unrounded f32 probabilities, so the LSE stays exact to
+// f32 rounding whatever chunk order the tiles are visited in.
 #include "internal.h"
 
 namespace chain {
@@ -139,51 +142,48 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
         if (range_live(ri)) { k0 = p.kr.beg[ri]; return true; }
       return false;
     };
-    int ri = 0, k0 = 0;
-    bool have = false;
-    for (; ri < p.kr.n; ++ri)
-      if (range_live(ri)) { k0 = p.kr.beg[ri]; have = true; break; }
-
-    uint4 kreg[LOADS], vreg[LOADS];
-    auto gload = [&](int r_i, int kk0) {
-      const int kend = p.kr.end[r_i];
+    struct Tl { int ri, k0; bool valid; };
+    auto first_tile = [&]() -> Tl {
+      for (int r = 0; r < p.kr.n; ++r)
+        if (range_live(r)) return Tl{r, p.kr.beg[r], true};
+      return Tl{0, 0, false};
+    };
+    auto next_tile = [&](Tl x) -> Tl {
+      if (!x.valid) return x;
+      int r = x.ri, k = x.k0;
+      return advance(r, k) ? Tl{r, k, true} : Tl{0, 0, false};
+    };
+    // global loads run two tiles ahead: tile j+2 is fetched into one register
+    // set while the set holding tile j+1 is written to LDS after tile j
+    uint4 kA[LOADS], vA[LOADS], kB[LOADS], vB[LOADS];
+    auto gload2 = [&](uint4 (&kr)[LOADS], uint4 (&vr)[LOADS], const Tl &x) {
+      const int kend = p.kr.end[x.ri];
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int cidx = tid + i * NW * 64;
         const int r = cidx / CPR, c8 = cidx % CPR;
-        const int key = kk0 + r;
+        const int key = x.k0 + r;
         if (key < kend) {
-          kreg[i] = *(const uint4 *)(kbase + (int64_t)key * p.k_ss + c8 * 8);
-          vreg[i] = *(const uint4 *)(vbase + (int64_t)key * p.v_ss + c8 * 8);
+          kr[i] = *(const uint4 *)(kbase + (int64_t)key * p.k_ss + c8 * 8);
+          vr[i] = *(const uint4 *)(vbase + (int64_t)key * p.v_ss + c8 * 8);
         } else {
-          kreg[i] = make_uint4(0, 0, 0, 0);
-          vreg[i] = make_uint4(0, 0, 0, 0);
+          kr[i] = make_uint4(0, 0, 0, 0);
+          vr[i] = make_uint4(0, 0, 0, 0);
         }
       }
     };
-    auto swrite = [&](int buf) {
+    auto swrite2 = [&](const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS], int buf) {
       __bf16 *ks = smem + buf * BUF;
       __bf16 *vs = ks + BN * LDK;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int cidx = tid + i * NW * 64;
         const int r = cidx / CPR, c8 = cidx % CPR;
-        *(uint4 *)(ks + r * LDK + c8 * 8) = kreg[i];
-        *(uint4 *)(vs + r * LDV + c8 * 8) = vreg[i];
+        *(uint4 *)(ks + r * LDK + c8 * 8) = kr[i];
+        *(uint4 *)(vs + r * LDV + c8 * 8) = vr[i];
       }
     };
-
-    if (have) {
-      gload(ri, k0);
-      swrite(0);
-    }
-    __syncthreads();
-    int buf = 0;
-    while (have) {
-      int nri = ri, nk0 = k0;
-      const bool more = advance(nri, nk0);
-      if (more) gload(nri, nk0);
-
+    auto compute = [&](const int ri, const int k0, const int buf) {
       // ---- compute on the staged tile
       const int off = p.kr.pos_off[ri];
       const int nvalid = min(BN, p.kr.end[ri] - k0);
@@ -279,12 +279,32 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
         }
       }
       __builtin_amdgcn_s_setprio(0);
-      if (more) swrite(buf ^ 1);
+    };
+
+    Tl w0 = first_tile(), w1 = next_tile(w0), w2 = next_tile(w1);
+    if (w0.valid) {
+      gload2(kA, vA, w0);
+      swrite2(kA, vA, 0);
+    }
+    if (w1.valid) gload2(kB, vB, w1);
+    __syncthreads();
+    int j = 0;
+    // x: register set holding w1 (written to LDS after this tile); y: set for w2
+    auto step = [&](uint4 (&kx)[LOADS], uint4 (&vx)[LOADS], uint4 (&ky)[LOADS], uint4 (&vy)[LOADS]) {
+      const int buf = j & 1;
+      if (w2.valid) gload2(ky, vy, w2);
+      compute(w0.ri, w0.k0, buf);
+      if (w1.valid) swrite2(kx, vx, buf ^ 1);
       __syncthreads();
-      buf ^= 1;
-      ri = nri;
-      k0 = nk0;
-      have = more;
+      w0 = w1;
+      w1 = w2;
+      w2 = next_tile(w2);
+      ++j;
+    };
+    while (w0.valid) {
+      step(kB, vB, kA, vA);
+      if (!w0.valid) break;
+      step(kA, vA, kB, vB);
     }
 
     // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
