@@ -274,3 +274,21 @@ def test_abi_errors_with_device_tensors():
     with pytest.raises(chain.ChainError) as e:
         chain.attn_fwd(q.transpose(2, 3), k, v)
     assert e.value.name in ("CHAIN_ERR_LAYOUT", "CHAIN_ERR_SHAPE")
+
+
+@pytest.mark.parametrize("C,D", [(3, 128), (5, 64), (16, 128), (1, 128), (8, 96)])
+def test_merge_part_counts_against_oracle(C, D):
+    """Compile-time part counts (1, 8, 16) and the generic path (3, 5), any D % 4."""
+    dev = device()
+    g = torch.Generator().manual_seed(60 + C)
+    o = torch.randn(C, 2, 3, 77, D, generator=g)
+    lse = torch.randn(C, 2, 3, 77, generator=g) * 3
+    lse[0, 1, 2, :10] = -math.inf            # some parts see nothing
+    lse[:, 0, 1, 5] = -math.inf              # a row that sees nothing at all
+    announce(f"merge C{C} D{D}")
+    mo, ml = chain.lse_merge(o.to(dev), lse.to(dev), out_dtype=torch.float32)
+    ro, rl = oracle.lse_merge(o.double().numpy(), lse.double().numpy())
+    assert max_abs(f64(mo), ro) <= 1e-5
+    assert max_abs(f64(ml), rl) <= 1e-5
+    mb, _ = chain.lse_merge(o.to(dev), lse.to(dev), out_dtype=torch.bfloat16)
+    assert max_abs(f64(mb), ro) <= 2e-2
