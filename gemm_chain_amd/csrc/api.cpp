@@ -67,7 +67,8 @@ int64_t numel(const chain_tensor &t) {
 // alignment the kernels need for the data pointer and every outer stride
 // (16 where rows are moved as 16-byte vectors, the element size where a
 // tensor is accessed element by element).
-chain_status check_tensor(const chain_tensor *t, const char *name, int ndim, int align = 16) {
+chain_status check_tensor(const chain_tensor *t, const char *name, int ndim, int align = 16,
+                          bool either_major = false) {
   if (t == nullptr) return fail(CHAIN_ERR_NULL, "%s: descriptor is NULL", name);
   if (t->ndim != ndim) return fail(CHAIN_ERR_SHAPE, "%s: expected %d dims, got %d", name, ndim, t->ndim);
   if (elem_size(t->dtype) == 0) return fail(CHAIN_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
@@ -77,14 +78,20 @@ chain_status check_tensor(const chain_tensor *t, const char *name, int ndim, int
   }
   if (numel(*t) == 0) return CHAIN_OK;
   if (t->data == nullptr) return fail(CHAIN_ERR_NULL, "%s: data is NULL", name);
-  if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
-    return fail(CHAIN_ERR_LAYOUT, "%s: last dimension must be contiguous (stride %lld)", name,
-                (long long)t->stride[ndim - 1]);
+  // The contiguous dimension: the last one, or (either_major, 2-D) the first.
+  int cdim = ndim - 1;
+  if (either_major && ndim == 2 && !(t->shape[1] <= 1 || t->stride[1] == 1) &&
+      (t->shape[0] <= 1 || t->stride[0] == 1))
+    cdim = 0;
+  if (t->shape[cdim] > 1 && t->stride[cdim] != 1)
+    return fail(CHAIN_ERR_LAYOUT, either_major ? "%s: neither dimension is contiguous"
+                                               : "%s: last dimension must be contiguous (stride %lld)",
+                name, (long long)t->stride[cdim]);
   const size_t es = elem_size(t->dtype);
   if (((uintptr_t)t->data) % align)
     return fail(CHAIN_ERR_ALIGN, "%s: data pointer not %d-byte aligned", name, align);
-  for (int i = 0; i < ndim - 1; ++i)
-    if (t->shape[i] > 1 && (t->stride[i] * (int64_t)es) % align)
+  for (int i = 0; i < ndim; ++i)
+    if (i != cdim && t->shape[i] > 1 && (t->stride[i] * (int64_t)es) % align)
       return fail(CHAIN_ERR_ALIGN, "%s: stride[%d] * %zu bytes not a multiple of %d", name, i, es, align);
   return CHAIN_OK;
 }
@@ -297,8 +304,8 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
                            const chain_tensor *O, int act, void *workspace, size_t ws_bytes,
                            void *stream) {
   TRY(check_tensor(X, "X", 2));
-  TRY(check_tensor(W1, "W1", 2));
-  TRY(check_tensor(W2, "W2", 2));
+  TRY(check_tensor(W1, "W1", 2, 16, true));
+  TRY(check_tensor(W2, "W2", 2, 16, true));
   TRY(check_tensor(O, "O", 2, O && O->dtype == CHAIN_F32 ? 4 : 2));
   if (W1->dtype != X->dtype || W2->dtype != X->dtype)
     return fail(CHAIN_ERR_DTYPE, "X, W1 and W2 must share one dtype");
@@ -327,17 +334,32 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
     if (overlap(H, *X) || overlap(H, *W1) || overlap(H, *W2) || overlap(H, *O))
       return fail(CHAIN_ERR_ALIAS, "workspace overlaps a tensor");
   }
+  // B strides: element (k, n) at b[k * b_sk + n * b_sn].  With one of the
+  // two extents 1 its stride is arbitrary; pick the layout the other implies.
+  auto b_strides = [](const chain_tensor &w, chain::GemmParams &g) {
+    const bool kmajor = !(w.shape[1] <= 1 || w.stride[1] == 1);
+    g.b_sk = kmajor ? 1 : (w.shape[0] <= 1 ? w.shape[1] : w.stride[0]);
+    g.b_sn = kmajor ? w.stride[1] : 1;
+  };
+  const size_t es = elem_size(X->dtype), oes = elem_size(O->dtype);
   chain::GemmParams g1{}, g2{};
   g1.a = X->data, g1.b = W1->data, g1.c = workspace;
-  g1.lda = X->stride[0], g1.ldb = W1->stride[0], g1.ldc = N;
+  g1.lda = X->stride[0], g1.ldc = N;
+  b_strides(*W1, g1);
   g1.M = (int32_t)M, g1.N = (int32_t)N, g1.K = (int32_t)K;
   g1.act = act;
   g1.c_f32 = X->dtype == CHAIN_F32;
+  g1.c_vec = (N * es) % (4 * es) == 0;   // workspace is 256-byte aligned
   g2.a = workspace, g2.b = W2->data, g2.c = O->data;
-  g2.lda = N, g2.ldb = W2->stride[0], g2.ldc = O->stride[0];
+  g2.lda = N, g2.ldc = O->stride[0];
+  b_strides(*W2, g2);
   g2.M = (int32_t)M, g2.N = (int32_t)K2, g2.K = (int32_t)N;
   g2.act = CHAIN_ACT_IDENTITY;
   g2.c_f32 = O->dtype == CHAIN_F32;
+  g2.c_vec = (uintptr_t)O->data % (4 * oes) == 0 && (M <= 1 || (O->stride[0] * oes) % (4 * oes) == 0);
+  const int64_t kMaxStride = int64_t(1) << 25;   // per-thread offsets within a tile stay 32-bit
+  for (const int64_t st : {g1.lda, g1.b_sk, g1.b_sn, g2.b_sk, g2.b_sn, g2.ldc})
+    if (st > kMaxStride) return fail(CHAIN_ERR_UNSUPPORTED, "row strides beyond 2^25 elements");
   hipError_t e = chain::launch_gemm(g1, X->dtype, (hipStream_t)stream);
   if (e == hipSuccess) e = chain::launch_gemm(g2, X->dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(CHAIN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));

@@ -3,32 +3,41 @@
 // METP article (abstract): O = f(A.B).C with f between two consecutive
 // products; for the MLP, A = X, B = W1, f = GeLU, C = W2 (TSP article, "Lo que
 // realmente significa plegar": one weight shard of the MLP ring).  This kernel
-// computes one product C = act(A.B) with A [M, K] and B [K, N] row-major; the
-// MLP runs it twice (act = GeLU into the workspace, then act = identity).
+// computes one product C = act(A.B) with A [M, K] row-major and B [K, N] in
+// either layout (n contiguous, or k contiguous: the transpose of a row-major
+// [N, K] weight, as linear layers store it); the MLP runs it twice (act = GeLU
+// into the workspace, then act = identity).
 //
-// bf16: tile 256 x 256 x 64 per 512-thread workgroup (8 waves, 2 per SIMD),
-// 2 x 4 waves of 128 x 64, each a 4 x 2 grid of v_mfma_f32_32x32x16_bf16 blocks
-// with f32 accumulation.  A and B tiles are staged row-major in LDS,
-// double-buffered through registers (one global fetch in flight while the
-// previous tile is consumed); the A operand is a plain 16-byte LDS read (8
-// consecutive k of one row, pitch BK + 8 so the reads of a wave spread over
-// all banks), the B operand (8 consecutive k of one column) comes from
-// ds_read_b64_tr_b16 at pitch BN + 32.  Rows/columns past M/N and k past K are
-// zero-filled.  The f32 path for f32 inputs keeps a 128 x 128 x 32 tile per
-// 256 threads with v_mfma_f32_32x32x2_f32.
+// bf16: one 256-thread workgroup per CU (one wave per SIMD) computes a
+// 256 x BN tile (BN = 256, 192 or 128, picked per launch so the tiles fill
+// whole rounds of the chip), 2 x 2 waves of 128 x BN/2, each a 4 x BN/64 grid
+// of v_mfma_f32_32x32x16_bf16 blocks whose f32 accumulators live in AGPRs.
+// Operands are swapped in the MFMA (it computes the transposed block) so a lane
+// ends up holding four consecutive output columns of one row: 8-byte stores.
+// A and B k-tiles of 64 are staged in LDS (two buffers) through registers; the
+// global fetch of tile k+2 is issued right after tile k+1 is written to LDS, so
+// it has most of a k-tile of MFMA work to arrive.  Within a tile the fragments
+// of k-step s+1 are read while the MFMAs of step s issue.  A (and a k-major B)
+// sits in LDS as [rows][64 + 8] (16-byte fragment reads hit distinct banks);
+// an n-major B sits as [64][BN' + 32] and is read with ds_read_b64_tr_b16.
+// Tiles that reach past M, N or K take a guarded load path (clamped address,
+// zero fill); all others take plain loads.  The f32 path for f32 inputs keeps
+// a 128 x 128 x 32 tile per 256 threads with v_mfma_f32_32x32x2_f32.
 #include "internal.h"
+
+#include <type_traits>
 
 namespace chain {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 128, TN = 128, TK = 32;
-constexpr int LDA = TK + 8;     // A tile pitch (elements)
-constexpr int LDB = TN + 8;     // B tile pitch (elements)
+constexpr int TM = 128, TN = 128, TK = 32;   // f32 path
 
 __device__ inline i16x4 ds_read_tr(const __bf16 *p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -44,133 +53,207 @@ __device__ inline float activate(float z, int act) {
   return z;
 }
 
-// bf16 path: 256 x 256 x 64 block tiles over eight waves (two per SIMD), each
-// wave computing 128 x 64 of C as 4 x 2 blocks of 32 x 32.  Every A fragment
-// read from LDS feeds two MFMAs and every B fragment four (0.75 KB of LDS reads
-// per MFMA).  A/B tiles are double-buffered in LDS; the global loads of stage
-// k+1 are in flight while stage k is computed, and within a stage the
-// fragments of k-step s+1 are read while the MFMAs of k-step s issue.
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WTM = 128, WTN = 64;        // wave tile
-constexpr int MB = WTM / 32, NB = WTN / 32;
-constexpr int LDAB = BK + 8;              // A pitch: conflict-free 16-byte reads
-constexpr int LDBB = BN + 32;             // B pitch: conflict-free transposing reads
-constexpr int GLOADS = BM * BK / 8 / 512; // 16-byte chunks per thread per operand
+constexpr int BM = 256, BK = 64;
+constexpr int LDA = BK + 8;        // pitch of k-contiguous stages
 
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2)))
+__device__ inline u32x4 ld16(const __bf16 *p) { return *(const u32x4 *)p; }
+
+// NBW = 32-column blocks per wave (BN = 64 * NBW); KMAJ: B has k contiguous.
+template <int NBW, bool KMAJ>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const GemmParams p) {
-  static_assert(BM * BK == BK * BN, "A and B stages split the same way");
-  __shared__ __attribute__((aligned(16))) __bf16 as[2][BM * LDAB];
-  __shared__ __attribute__((aligned(16))) __bf16 bs[2][BK * LDBB];
+  constexpr int BN = 64 * NBW, WTN = 32 * NBW;
+  constexpr int LDBN = ((BN + 127) / 128) * 128 + 32;   // n-major pitch: conflict-free tr reads
+  constexpr int BSZ = KMAJ ? BN * LDA : BK * LDBN;
+  constexpr int AL = BM * BK / 8 / 256;                  // 16-byte chunks per thread
+  constexpr int BL = BN * BK / 8 / 256;
+  constexpr int BCH = BN / 8;                            // chunks per n-major B row
+  __shared__ __attribute__((aligned(16))) __bf16 as[2][BM * LDA];
+  __shared__ __attribute__((aligned(16))) __bf16 bs[2][BSZ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
 
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
   const int tile = xcd_remap(blockIdx.x, tiles);
   const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
-
   const __bf16 *A = (const __bf16 *)p.a;
   const __bf16 *B = (const __bf16 *)p.b;
-  uint4 ar[GLOADS], br[GLOADS];
-  auto gload = [&](int k0) {
+  const int64_t ldb = KMAJ ? p.b_sn : p.b_sk;
+  const int nk = (p.K + BK - 1) / BK;
+  const int nk_plain = (m0 + BM <= p.M && n0 + BN <= p.N) ? p.K / BK : 0;
+
+  // Chunk c = tid + 256 i of a stage: A row (c >> 3) = (tid >> 3) + 32 i, k
+  // chunk c & 7 = tid & 7; likewise for a k-major B.  An n-major B row holds
+  // BCH chunks.  Per-thread byte offsets stay 32-bit; the per-i part is uniform.
+  const char *Ab = (const char *)A, *Bb = (const char *)B;
+  const uint32_t a_off = (uint32_t)((tid >> 3) * p.lda + (tid & 7) * 8) * 2u;
+  const uint32_t b_off = KMAJ ? (uint32_t)((tid >> 3) * ldb + (tid & 7) * 8) * 2u
+                              : (uint32_t)((tid / BCH) * ldb + (tid % BCH) * 8) * 2u;
+  u32x4 ar[AL], br[BL];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+    if (kt < nk_plain) {
 #pragma unroll
-    for (int i = 0; i < GLOADS; ++i) {
-      const int c = tid + 512 * i;
-      const int ra = c >> 3, ka = (c & 7) * 8;            // A: 256 rows x 8 chunks
-      const int gm = m0 + ra, gk = k0 + ka;
-      ar[i] = (gm < p.M && gk < p.K) ? *(const uint4 *)(A + (int64_t)gm * p.lda + gk)
-                                     : make_uint4(0, 0, 0, 0);
-      const int kb = c >> 5, nb = (c & 31) * 8;           // B: 64 rows x 32 chunks
-      const int gk2 = k0 + kb, gn = n0 + nb;
-      br[i] = (gk2 < p.K && gn < p.N) ? *(const uint4 *)(B + (int64_t)gk2 * p.ldb + gn)
-                                      : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < AL; ++i) {
+        const char *base = Ab + ((int64_t)(m0 + 32 * i) * p.lda + k0) * 2;
+        ar[i] = *(const u32x4 *)(base + a_off);
+      }
+#pragma unroll
+      for (int i = 0; i < BL; ++i) {
+        const int c = tid + 256 * i;
+        if (KMAJ) {
+          const char *base = Bb + ((int64_t)(n0 + 32 * i) * ldb + k0) * 2;
+          br[i] = *(const u32x4 *)(base + b_off);
+        } else if (256 % BCH == 0) {
+          const char *base = Bb + ((int64_t)(k0 + (256 / BCH) * i) * ldb + n0) * 2;
+          br[i] = *(const u32x4 *)(base + b_off);
+        } else {
+          br[i] = ld16(B + (int64_t)(k0 + c / BCH) * ldb + n0 + (c % BCH) * 8);
+        }
+      }
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < AL; ++i) {
+        const int c = tid + 256 * i;
+        const int gm = m0 + (c >> 3), gk = k0 + (c & 7) * 8;
+        const bool ok = gm < p.M && gk < p.K;
+        const u32x4 v = ld16(ok ? A + (int64_t)gm * p.lda + gk : A);
+        ar[i] = ok ? v : z;
+      }
+#pragma unroll
+      for (int i = 0; i < BL; ++i) {
+        const int c = tid + 256 * i;
+        int gk, gn;
+        if (KMAJ) gn = n0 + (c >> 3), gk = k0 + (c & 7) * 8;
+        else gk = k0 + c / BCH, gn = n0 + (c % BCH) * 8;
+        const bool ok = gk < p.K && gn < p.N;
+        const u32x4 v = ld16(ok ? (KMAJ ? B + (int64_t)gn * ldb + gk : B + (int64_t)gk * ldb + gn) : B);
+        br[i] = ok ? v : z;
+      }
     }
   };
   auto swrite = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < GLOADS; ++i) {
-      const int c = tid + 512 * i;
-      *(uint4 *)(&as[buf][(c >> 3) * LDAB + (c & 7) * 8]) = ar[i];
-      *(uint4 *)(&bs[buf][(c >> 5) * LDBB + (c & 31) * 8]) = br[i];
+    for (int i = 0; i < AL; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4 *)(&as[buf][(c >> 3) * LDA + (c & 7) * 8]) = ar[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int c = tid + 256 * i;
+      if (KMAJ) *(u32x4 *)(&bs[buf][(c >> 3) * LDA + (c & 7) * 8]) = br[i];
+      else *(u32x4 *)(&bs[buf][(c / BCH) * LDBN + (c % BCH) * 8]) = br[i];
     }
   };
 
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
-
+  struct Frags {
+    bf16x8 a[4], b[NBW];
+  };
   const int trow = (lane & 15) >> 2;
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  auto frags = [&](int buf, int ks, bf16x8 (&a)[MB], bf16x8 (&b)[NB]) {
+  auto frags = [&](int buf, int ks, Frags &f) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-      a[i] = *(const bf16x8 *)(&as[buf][(wm * WTM + i * 32 + l32) * LDAB + ks * 16 + 8 * h2]);
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = *(const bf16x8 *)(&as[buf][(wm * 128 + i * 32 + l32) * LDA + ks * 16 + 8 * h2]);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const __bf16 *src = &bs[buf][(ks * 16 + 8 * h2 + trow) * LDBB + wn * WTN + j * 32 + tcol];
-      const i16x4 lo = ds_read_tr(src);
-      const i16x4 hi = ds_read_tr(src + 4 * LDBB);
-      b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int j = 0; j < NBW; ++j) {
+      if (KMAJ) {
+        f.b[j] = *(const bf16x8 *)(&bs[buf][(wn * WTN + j * 32 + l32) * LDA + ks * 16 + 8 * h2]);
+      } else {
+        const __bf16 *src = &bs[buf][(ks * 16 + 8 * h2 + trow) * LDBN + wn * WTN + j * 32 + tcol];
+        const i16x4 lo = ds_read_tr(src);
+        const i16x4 hi = ds_read_tr(src + 4 * LDBN);
+        f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     }
   };
 
-  const int nk = (p.K + BK - 1) / BK;
+  // acc[i][j] holds the transposed 32 x 32 block: lane (h2, l32) has row
+  // m = l32 and columns n = 8 * (r / 4) + 4 * h2 + r % 4 in element r.
+  f32x16 acc[4][NBW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](const Frags &f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+
+  Frags f0, f1;
   gload(0);
   swrite(0);
+  if (nk > 1) gload(1);
   __syncthreads();
+  frags(0, 0, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload((kt + 1) * BK);
-    bf16x8 a0[MB], b0[NB], a1[MB], b1[NB];
-    frags(buf, 0, a0, b0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks += 2) {
-      frags(buf, ks + 1, a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks + 2 < BK / 16) frags(buf, ks + 2, a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    const int cur = kt & 1, nxt = cur ^ 1;
+    frags(cur, 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(cur, 2, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      swrite(nxt);
+      if (kt + 2 < nk) gload(kt + 2);
     }
-    if (more) swrite(buf ^ 1);
+    frags(cur, 3, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    if (kt + 1 < nk) frags(nxt, 0, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // epilogue: lane owns column l32 of each 32x32 block, rows 8*(r/4) + 4*h2 + r%4
+  auto store_all = [&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int gm = m0 + wm * 128 + i * 32 + l32;
+      if (gm >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int gn = n0 + wn * WTN + j * 32 + l32;
-      if (gn >= p.N) continue;
+      for (int j = 0; j < NBW; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gm = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (gm >= p.M) continue;
-        const float v = activate(acc[i][j][r], p.act);
-        if (p.c_f32) ((float *)p.c)[(int64_t)gm * p.ldc + gn] = v;
-        else ((__bf16 *)p.c)[(int64_t)gm * p.ldc + gn] = (__bf16)v;
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
+          if (gn >= p.N) continue;   // N % 4 == 0: the four columns are all in or all out
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
+          const int64_t off = (int64_t)gm * p.ldc + gn;
+          if (p.c_f32) {
+            float *c = (float *)p.c + off;
+            if (p.c_vec) *(f32x4 *)c = v;
+            else c[0] = v[0], c[1] = v[1], c[2] = v[2], c[3] = v[3];
+          } else {
+            __bf16 *c = (__bf16 *)p.c + off;
+            const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            if (p.c_vec) *(bf16x4 *)c = w;
+            else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
+          }
+        }
     }
+  };
+  if (p.act == CHAIN_ACT_GELU_ERF) store_all(std::integral_constant<int, CHAIN_ACT_GELU_ERF>{});
+  else if (p.act == CHAIN_ACT_GELU_TANH) store_all(std::integral_constant<int, CHAIN_ACT_GELU_TANH>{});
+  else store_all(std::integral_constant<int, CHAIN_ACT_IDENTITY>{});
 }
 
-// f32 inputs: same tiles on v_mfma_f32_32x32x2_f32 (A: lane holds A[m][k0 + h2],
-// B: lane holds B[k0 + h2][n]); exact f32 products, f32 accumulation.
+// f32 inputs: 128 x 128 x 32 tiles on v_mfma_f32_32x32x2_f32 (A: lane holds
+// A[m][k0 + h2], B: lane holds B[k0 + h2][n]); exact f32 products, f32
+// accumulation.
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
   __shared__ float as[TM][TK + 1];
   __shared__ float bs[TK][TN + 4];
@@ -195,7 +278,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
     }
     for (int e = tid; e < TK * TN; e += 256) {
       const int r = e / TN, c = e % TN;
-      bs[r][c] = (k0 + r < p.K && n0 + c < p.N) ? B[(int64_t)(k0 + r) * p.ldb + n0 + c] : 0.f;
+      bs[r][c] = (k0 + r < p.K && n0 + c < p.N)
+                     ? B[(int64_t)(k0 + r) * p.b_sk + (int64_t)(n0 + c) * p.b_sn]
+                     : 0.f;
     }
     __syncthreads();
 #pragma unroll 4
@@ -230,12 +315,51 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
     }
 }
 
+template <int NBW, bool KMAJ>
+void launch_bf16(const GemmParams &p, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * NBW - 1) / (64 * NBW));
+  hipLaunchKernelGGL((gemm_bf16_kernel<NBW, KMAJ>), dim3(tiles), dim3(256), 0, stream, p);
+}
+
+template <bool KMAJ>
+void launch_bf16_width(const GemmParams &p, int nbw, hipStream_t stream) {
+  if (nbw == 4) launch_bf16<4, KMAJ>(p, stream);
+  else if (nbw == 3) launch_bf16<3, KMAJ>(p, stream);
+  else launch_bf16<2, KMAJ>(p, stream);
+}
+
+int compute_units() {
+  static thread_local int dev_cached = -1, cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return cus;
+  if (dev != dev_cached) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+    dev_cached = dev;
+  }
+  return cus;
+}
+
 }  // namespace
+
+// Tile width for the bf16 path: the one that minimises rounds x tile width
+// (one workgroup per CU; the time of a tile grows with its width).
+int gemm_bf16_block_cols(int M, int N, int cus) {
+  int best = 4;
+  int64_t best_cost = INT64_MAX;
+  for (int nbw = 4; nbw >= 2; --nbw) {
+    const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + 64 * nbw - 1) / (64 * nbw));
+    const int64_t cost = ((tiles + cus - 1) / cus) * nbw;
+    if (cost < best_cost) best = nbw, best_cost = cost;
+  }
+  return best;
+}
 
 hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
   if (dtype == CHAIN_BF16) {
-    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tiles), dim3(512), 0, stream, p);
+    const int nbw = gemm_bf16_block_cols(p.M, p.N, compute_units());
+    if (p.b_sk == 1) launch_bf16_width<true>(p, nbw, stream);
+    else launch_bf16_width<false>(p, nbw, stream);
   } else {
     const int tiles = ((p.M + TM - 1) / TM) * ((p.N + TN - 1) / TN);
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, p);

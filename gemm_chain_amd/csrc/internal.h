@@ -157,13 +157,14 @@ struct MergeParams {
 };
 
 struct GemmParams {
-  const void *a;      // [M, K]
-  const void *b;      // [K, N]
-  void *c;            // [M, N]
-  int64_t lda, ldb, ldc;
+  const void *a;      // [M, K], row stride lda (k contiguous)
+  const void *b;      // [K, N]: element (k, n) at b[k * b_sk + n * b_sn]; b_sk == 1 or b_sn == 1
+  void *c;            // [M, N], row stride ldc (n contiguous)
+  int64_t lda, b_sk, b_sn, ldc;
   int32_t M, N, K;
   int32_t act;        // chain_act
   int32_t c_f32;      // 1: C is f32, 0: C is bf16
+  int32_t c_vec;      // 1: C rows allow 4-element vector stores (aligned base and ldc)
 };
 
 // Launchers (defined in the .hip files).  Each returns the launch's hipError_t.

@@ -31,14 +31,16 @@
  *   workspace).  The library never allocates or frees device memory and keeps
  *   no state between calls other than a thread-local error message.
  * - Layout: chain_tensor gives shape and strides in ELEMENTS; the last
- *   dimension must be contiguous (stride 1), other strides are free (>= 0).
+ *   dimension must be contiguous (stride 1), other strides are free (>= 0);
+ *   the MLP weights may instead have their first dimension contiguous.
  *   Attention tensors are [B, H, S, D]; LSE tensors are [B, H, S]; partial
  *   tensors carry a leading chunk dimension [C, B, H, S, D] / [C, B, H, S].
  * - Alignment (CHAIN_ERR_ALIGN otherwise): for tensors whose rows the kernels
  *   move as 16-byte vectors (Q, K, V, attention O, O_parts, X, W1, W2) the
- *   data pointer and every outer stride times the element size must be
- *   multiples of 16 bytes; 8 bytes for a bf16 merge output; LSE tensors and
- *   the MLP output only need element alignment.
+ *   data pointer and every non-contiguous stride times the element size must
+ *   be multiples of 16 bytes; 8 bytes for a bf16 merge output; LSE tensors and
+ *   the MLP output only need element alignment (an MLP output whose pointer
+ *   and row stride are multiples of 4 elements is written with vector stores).
  * - Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
  *   only enqueue work on it and return at once; results are visible after the
  *   caller synchronises the stream.  Calls are reentrant; concurrent calls on
@@ -179,13 +181,19 @@ chain_status chain_lse_merge(const chain_tensor *O_parts, const chain_tensor *LS
  * chain_mlp_fwd -- O = act(X.W1).W2 (METP article, abstract; TSP article: one
  * weight shard of the MLP ring).
  *
- *   X  [M, K]   bf16 or f32 (input)      W1 [K, N]  same dtype (input)
- *   W2 [N, K2]  same dtype (input)       O  [M, K2] bf16 or f32 (output)
+ *   X  [M, K]   bf16 or f32 (input, row-major)
+ *   W1 [K, N]   same dtype (input)       W2 [N, K2]  same dtype (input)
+ *               Each weight is row-major (stride (ld, 1)) or column-major
+ *               (stride (1, ld)): the transpose of a row-major [N, K] array,
+ *               the layout linear layers keep their weights in.  Column-major
+ *               weights are the faster form (both operands stream along k).
+ *   O  [M, K2]  bf16 or f32 (output, row-major)
  *   workspace   device buffer of at least chain_mlp_workspace_bytes(M, N, dtype)
  *               bytes, 256-byte aligned; holds H = act(X.W1) in the input dtype
  *               (bf16 H is rounded to nearest even, as the second product's
  *               MFMA operand).  Owned by the caller; contents are scratch.
- * Accumulation is f32.  K, N, K2 must be multiples of 8.
+ * Accumulation is f32.  K, N, K2 must be multiples of 8 and row strides at
+ * most 2^25 elements (CHAIN_ERR_UNSUPPORTED otherwise).
  */
 chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1,
                            const chain_tensor *W2, const chain_tensor *O, int act,

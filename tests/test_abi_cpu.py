@@ -160,6 +160,18 @@ def test_merge_and_mlp_validation_codes(lib):
     W1f = td([256, 128], chain.F32, FAKE + 2 ** 30)
     assert lib.chain_mlp_fwd(P(X), P(W1f), P(W2), P(Om), 0, ws, need, None) == CODES["CHAIN_ERR_DTYPE"]
     assert lib.chain_mlp_fwd(P(X), P(W1), P(W2), P(Om), 0, FAKE + 256, need, None) == CODES["CHAIN_ERR_ALIAS"]
+    # Weights may be row- or column-major, but one dimension must be contiguous.
+    W1s = td([256, 128], chain.BF16, FAKE + 2 ** 30, stride=[256, 2])
+    assert lib.chain_mlp_fwd(P(X), P(W1s), P(W2), P(Om), 0, ws, need, None) == CODES["CHAIN_ERR_LAYOUT"]
+    W1c = td([256, 128], chain.BF16, FAKE + 2 ** 30, stride=[1, 264])   # column-major, aligned
+    W1m = td([256, 128], chain.BF16, FAKE + 2 ** 30, stride=[1, 257])   # column stride not 16-byte
+    assert lib.chain_mlp_fwd(P(X), P(W1m), P(W2), P(Om), 0, ws, need, None) == CODES["CHAIN_ERR_ALIGN"]
+    W1w = td([256, 128], chain.BF16, FAKE + 2 ** 40, stride=[1, 2 ** 25 + 8])
+    assert lib.chain_mlp_fwd(P(X), P(W1w), P(W2), P(Om), 0, ws, need, None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    # A valid column-major weight passes validation (the error comes from elsewhere).
+    assert lib.chain_mlp_fwd(P(X), P(W1c), P(W2), P(Om), 7, ws, need, None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    Xc = td([512, 256], chain.BF16, FAKE, stride=[1, 512])               # X must be row-major
+    assert lib.chain_mlp_fwd(P(Xc), P(W1), P(W2), P(Om), 0, ws, need, None) == CODES["CHAIN_ERR_LAYOUT"]
 
 
 @pytest.mark.parametrize("S,P", [(32, 1), (256, 8), (32768, 8), (96, 3)])

@@ -70,3 +70,53 @@ def test_mlp_zero_input():
     announce("mlp X = 0")
     o = chain.mlp_fwd(x, w1.to(dev), w2.to(dev))
     assert torch.all(o == 0)
+
+
+def _kmajor(w):
+    """The same [K, N] values stored column-major (a row-major [N, K] array, transposed)."""
+    return w.t().contiguous().t()
+
+
+# On a 256-CU device these shapes select each bf16 tile width: N = 1376 over
+# 63 row tiles takes 192-wide tiles, N = 4096 takes 256-wide ones, small
+# problems 128-wide.  M, N or K is ragged in each.
+@pytest.mark.parametrize("M,K,N,K2", [
+    (16000, 4096, 1376, 4096),
+    (4000, 1376, 4096, 264),
+    (300, 200, 136, 264),
+])
+def test_mlp_weight_layouts_agree_and_match_oracle(M, K, N, K2):
+    dev = device()
+    x, w1, w2 = gen_mlp(M, K, N, K2, dtype="bf16", amp_x=1.0, amp_w=0.02, seed=60 + M % 97)
+    xd, w1d, w2d = x.to(dev), w1.to(dev), w2.to(dev)
+    announce(f"mlp layouts M{M} K{K} N{N} K2{K2}")
+    o_row = chain.mlp_fwd(xd, w1d, w2d, act="gelu_erf")
+    o_col = chain.mlp_fwd(xd, _kmajor(w1d), _kmajor(w2d), act="gelu_erf")
+    o_mix = chain.mlp_fwd(xd, _kmajor(w1d), w2d, act="gelu_erf")
+    torch.cuda.synchronize()
+    # Same products in the same k order whatever the weight layout.
+    assert torch.equal(o_row, o_col) and torch.equal(o_row, o_mix)
+    rows = sample_rows(M, 96, 7, extra=(0, M - 1, min(M - 1, 255), min(M - 1, 256)))
+    ref = oracle.mlp(f64(x[rows]), f64(w1), f64(w2), "gelu_erf")
+    err = max_abs(f64(o_col.cpu()[rows]), ref)
+    print(f"max-abs {err:.3e} over {len(rows)} rows")
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_mlp_output_row_stride_not_vector_aligned(out_dtype):
+    """An output whose row stride is not a multiple of 4 elements (element stores)."""
+    dev = device()
+    M, K, N, K2 = 260, 128, 136, 200
+    x, w1, w2 = gen_mlp(M, K, N, K2, dtype="bf16", amp_x=1.0, amp_w=0.05, seed=70)
+    xd, w1d, w2d = x.to(dev), _kmajor(w1.to(dev)), w2.to(dev)
+    announce(f"mlp strided output {out_dtype}")
+    base = torch.full((M, K2 + 2), 7.0, dtype=out_dtype, device=dev)
+    o = base[:, :K2]
+    chain.mlp_fwd(xd, w1d, w2d, act="gelu_tanh", out=o)
+    dense = chain.mlp_fwd(xd, w1d, w2d, act="gelu_tanh", out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o, dense)
+    assert torch.all(base[:, K2:] == 7.0)
+    ref = oracle.mlp(f64(x), f64(w1), f64(w2), "gelu_tanh")
+    assert max_abs(f64(o), ref) <= TOL_BF16
