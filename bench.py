@@ -177,10 +177,16 @@ def secondary(torch, chain, steps):
                                             amp_w=w.amp_w, seed=w.seed))
     o = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(chain.mlp_workspace_bytes(w.M, w.N), dtype=torch.uint8, device=dev)
-    ms = time_region(torch, lambda: chain.mlp_fwd(x, w1, w2, act=w.act, out=o, workspace=ws), steps, 2, stream)
+    # Weights as linear layers store them ([out, in] row-major, i.e. column-major
+    # [in, out]: k contiguous), and as row-major [in, out] arrays.
+    w1c, w2c = w1.t().contiguous().t(), w2.t().contiguous().t()
     flops = 4.0 * w.M * w.K * w.N
-    out[w.name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-                   "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    res = {}
+    for tag, (a, b) in (("", (w1c, w2c)), ("_rowmajor_w", (w1, w2))):
+        ms = time_region(torch, lambda: chain.mlp_fwd(x, a, b, act=w.act, out=o, workspace=ws), steps, 2, stream)
+        res.update({"ms" + tag: round(ms, 4), "tflops" + tag: round(flops / ms / 1e9, 1),
+                    "frac_peak" + tag: round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)})
+    out[w.name] = res
     return out
 
 
