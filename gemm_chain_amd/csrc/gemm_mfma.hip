@@ -251,6 +251,212 @@ void gemm_bf16_kernel(const GemmParams p) {
   else store_all(std::integral_constant<int, CHAIN_ACT_IDENTITY>{});
 }
 
+// ---- k-contiguous A and B: direct-to-LDS stage ring ------------------------
+//
+// Same 256 x BN tile, waves and MFMA blocks as above, but the operands never
+// pass through registers: each wave-level global_load_lds_dwordx4 drops 64
+// lanes x 16 bytes (16 rows x 32 k) straight into LDS.  k-tiles of 32 sit in
+// a ring of four stages and are fetched three stages ahead, so 3 x (256 + BN)
+// x 64 bytes per CU are in flight while a stage is computed.  A row of a stage
+// is 64 bytes (four 16-byte chunks); chunk c of row r is stored at position
+// c ^ ((r >> 2) & 3), which puts the 16-byte fragment reads of 16 consecutive
+// rows on 16 distinct bank groups (the load side chooses which global chunk
+// each lane fetches, so the swizzle costs nothing).  Rows past M or N read the
+// last valid row (their results are never stored); chunks past K read a valid
+// chunk and are overwritten with zeros once they have landed.
+constexpr int DBK = 32;   // k per stage
+constexpr int DST = 4;    // stages in the ring
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+template <int NBW>
+__device__ __forceinline__ void gemm_bf16_dtl(const GemmParams &p) {
+  constexpr int BN = 64 * NBW, WTN = 32 * NBW;
+  constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int LA = 4, LB = NBW, L = LA + LB;   // 1 KB loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) char lds[DST * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Tile order: groups of 4 row blocks x all column blocks, row block fastest,
+  // so the 32 tiles an XCD runs at once cover 4 x 8 blocks.
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  constexpr int GM = 4;
+  const int g = t / (GM * tiles_n), fm = g * GM;
+  const int gmn = min(GM, tiles_m - fm), loc = t - g * GM * tiles_n;
+  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * BN;
+
+  // Lane i of a load fetches row i >> 2 of its 16-row block, logical chunk lc.
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const __bf16 *A = (const __bf16 *)p.a;
+  const __bf16 *B = (const __bf16 *)p.b;
+  int64_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int q = 0; q < LA; ++q)
+    a_off[q] = (int64_t)min(m0 + 16 * (wave * LA + q) + (lane >> 2), p.M - 1) * p.lda + 8 * lc;
+#pragma unroll
+  for (int q = 0; q < LB; ++q)
+    b_off[q] = (int64_t)min(n0 + 16 * (wave * LB + q) + (lane >> 2), p.N - 1) * p.b_sn + 8 * lc;
+  const int nk = (p.K + DBK - 1) / DBK;
+
+  // Stage kt >= nk (issued so that every loop iteration has the same shape)
+  // fetches valid data into a ring buffer nobody reads.
+  auto issue = [&](int kt) {
+    char *sb = lds + (kt & (DST - 1)) * STAGE;
+    const int k0 = kt * DBK;
+    // In the K tail a chunk past K fetches k = K - 8 of its row instead.
+    const int kk = k0 + DBK <= p.K ? k0 : min(k0 + 8 * lc, p.K - 8) - 8 * lc;
+#pragma unroll
+    for (int q = 0; q < LA; ++q)
+      __builtin_amdgcn_global_load_lds(A + a_off[q] + kk, sb + (wave * LA + q) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < LB; ++q)
+      __builtin_amdgcn_global_load_lds(B + b_off[q] + kk, sb + A_BYTES + (wave * LB + q) * 1024, 16, 0, 0);
+  };
+  // After stage kt (the K tail) has landed: zero the chunks past K.
+  auto zero_tail = [&](int kt) {
+    if (kt * DBK + 8 * lc >= p.K) {
+      char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < LA; ++q) *(u32x4 *)(sb + (wave * LA + q) * 1024) = z;
+#pragma unroll
+      for (int q = 0; q < LB; ++q) *(u32x4 *)(sb + A_BYTES + (wave * LB + q) * 1024) = z;
+    }
+  };
+  // Wait until this wave's loads of stage s have landed (stages s+1 and s+2
+  // may still be in flight), then zero the K tail if stage s holds it.
+  auto wait_stage = [&](int s) {
+    wait_vmcnt<2 * L>();
+    if (s < nk && s * DBK + DBK > p.K) zero_tail(s);
+  };
+
+  struct Frags {
+    bf16x8 a[4], b[NBW];
+  };
+  const int sx = (l32 >> 2) & 3;
+  const int pc0 = (h2 ^ sx) * 16, pc1 = ((2 + h2) ^ sx) * 16;
+  const int rowa = (wm * 128 + l32) * 64, rowb = A_BYTES + (wn * WTN + l32) * 64;
+  auto frags = [&](int kt, int ks, Frags &f) {
+    const char *sb = lds + (kt & (DST - 1)) * STAGE + (ks ? pc1 : pc0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *(const bf16x8 *)(sb + rowa + i * 2048);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) f.b[j] = *(const bf16x8 *)(sb + rowb + j * 2048);
+  };
+
+  f32x16 acc[4][NBW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](const Frags &f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+
+  // One iteration: [issue stage kt+3 | read fragments of k-step 1 | MFMAs of
+  // k-step 0] interleaved one MFMA to one memory instruction, then wait for
+  // stage kt+1 and barrier, then [read k-step 0 of stage kt+1 | MFMAs of
+  // k-step 1], again interleaved.  With one wave per SIMD nothing else can
+  // issue MFMAs while a wave issues loads, so they go between its MFMAs.
+  Frags f0, f1;
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < DST - 1; ++s) issue(s);
+    wait_stage(0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    frags(0, 0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      // f0, read after the previous barrier, has had a block of MFMAs to land;
+      // waiting for it here keeps the compiler from waiting on f1 below.
+      wait_lgkmcnt0();
+      __builtin_amdgcn_sched_barrier(0);
+      // Stage kt+3 reuses the buffer of stage kt-1, whose last reads finished
+      // before the previous barrier.
+      issue(kt + DST - 1);
+      frags(kt, 1, f1);
+      mfmas(f0);
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load (to LDS)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBW - L, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_stage(kt + 1);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      frags(kt + 1, 0, f0);   // past the last stage: an unused read of a ring buffer
+      mfmas(f1);
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBW - L, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
+  }
+
+  auto store_all = [&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gm = m0 + wm * 128 + i * 32 + l32;
+      if (gm >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
+          if (gn >= p.N) continue;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
+          const int64_t off = (int64_t)gm * p.ldc + gn;
+          if (p.c_f32) {
+            float *c = (float *)p.c + off;
+            if (p.c_vec) *(f32x4 *)c = v;
+            else c[0] = v[0], c[1] = v[1], c[2] = v[2], c[3] = v[3];
+          } else {
+            __bf16 *c = (__bf16 *)p.c + off;
+            const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            if (p.c_vec) *(bf16x4 *)c = w;
+            else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
+          }
+        }
+    }
+  };
+  if (p.act == CHAIN_ACT_GELU_ERF) store_all(std::integral_constant<int, CHAIN_ACT_GELU_ERF>{});
+  else if (p.act == CHAIN_ACT_GELU_TANH) store_all(std::integral_constant<int, CHAIN_ACT_GELU_TANH>{});
+  else store_all(std::integral_constant<int, CHAIN_ACT_IDENTITY>{});
+}
+
+// One plain kernel per tile width (the body is a template).
+#define CHAIN_DTL_KERNEL(NBW)                                                              \
+  __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) \
+  void gemm_bf16_dtl_kernel_##NBW(const GemmParams p) { gemm_bf16_dtl<NBW>(p); }
+CHAIN_DTL_KERNEL(2)
+CHAIN_DTL_KERNEL(3)
+CHAIN_DTL_KERNEL(4)
+#undef CHAIN_DTL_KERNEL
+
 // f32 inputs: 128 x 128 x 32 tiles on v_mfma_f32_32x32x2_f32 (A: lane holds
 // A[m][k0 + h2], B: lane holds B[k0 + h2][n]); exact f32 products, f32
 // accumulation.
@@ -328,6 +534,13 @@ void launch_bf16_width(const GemmParams &p, int nbw, hipStream_t stream) {
   else launch_bf16<2, KMAJ>(p, stream);
 }
 
+void launch_dtl(const GemmParams &p, int nbw, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * nbw - 1) / (64 * nbw));
+  if (nbw == 4) hipLaunchKernelGGL(gemm_bf16_dtl_kernel_4, dim3(tiles), dim3(256), 0, stream, p);
+  else if (nbw == 3) hipLaunchKernelGGL(gemm_bf16_dtl_kernel_3, dim3(tiles), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(gemm_bf16_dtl_kernel_2, dim3(tiles), dim3(256), 0, stream, p);
+}
+
 int compute_units() {
   static thread_local int dev_cached = -1, cus = 256;
   int dev = 0;
@@ -356,10 +569,14 @@ int gemm_bf16_block_cols(int M, int N, int cus) {
 }
 
 hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
   if (dtype == CHAIN_BF16) {
     const int nbw = gemm_bf16_block_cols(p.M, p.N, compute_units());
-    if (p.b_sk == 1) launch_bf16_width<true>(p, nbw, stream);
-    else launch_bf16_width<false>(p, nbw, stream);
+    if (p.b_sk == 1) {
+      launch_dtl(p, nbw, stream);
+    } else {
+      launch_bf16_width<false>(p, nbw, stream);
+    }
   } else {
     const int tiles = ((p.M + TM - 1) / TM) * ((p.N + TN - 1) / TN);
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, p);
