@@ -187,11 +187,13 @@ void gemm_bf16_kernel(const GemmParams p) {
   };
 
   Frags f0, f1;
-  gload(0);
-  swrite(0);
-  if (nk > 1) gload(1);
-  __syncthreads();
-  frags(0, 0, f0);
+  if (nk > 0) {   // K = 0: nothing to load (the operands may have no storage)
+    gload(0);
+    swrite(0);
+    if (nk > 1) gload(1);
+    __syncthreads();
+    frags(0, 0, f0);
+  }
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1, nxt = cur ^ 1;
     frags(cur, 1, f1);

@@ -120,3 +120,23 @@ def test_mlp_output_row_stride_not_vector_aligned(out_dtype):
     assert torch.all(base[:, K2:] == 7.0)
     ref = oracle.mlp(f64(x), f64(w1), f64(w2), "gelu_tanh")
     assert max_abs(f64(o), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kmajor", [False, True])
+def test_mlp_empty_inner_dimensions(dtype, kmajor):
+    """K = 0 gives H = act(0) = 0 and N = 0 an empty intermediate: O = 0 either way."""
+    dev = device()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    M, K2 = 300, 264
+    announce(f"mlp empty inner dims {dtype} kmajor={kmajor}")
+    for K, N in ((0, 136), (128, 0)):
+        x = torch.randn(M, K, device=dev).to(tdt)
+        w1 = torch.randn(K, N, device=dev).to(tdt)
+        w2 = torch.randn(N, K2, device=dev).to(tdt)
+        if kmajor:
+            w1, w2 = _kmajor(w1), _kmajor(w2)
+        o = torch.full((M, K2), 5.0, dtype=tdt, device=dev)
+        chain.mlp_fwd(x, w1, w2, act="gelu_erf", out=o)
+        torch.cuda.synchronize()
+        assert torch.all(o == 0), (K, N)
