@@ -151,6 +151,12 @@ chain_status check_attn(const chain_tensor *Q, const chain_tensor *K, const chai
   if (D != 64 && D != 128) return fail(CHAIN_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)D);
   if (Sq > INT32_MAX / 2 || K->shape[2] > INT32_MAX / 2 || B * Hq > INT32_MAX)
     return fail(CHAIN_ERR_UNSUPPORTED, "sizes beyond 2^30 rows");
+  // The bf16 kernels address one head's key/value rows with 32-bit byte offsets.
+  if (Q->dtype == CHAIN_BF16 && K->shape[2] > 0) {
+    const int64_t last = K->shape[2] - 1;
+    if ((last * K->stride[2] + D) * 2 > INT32_MAX || (last * V->stride[2] + D) * 2 > INT32_MAX)
+      return fail(CHAIN_ERR_UNSUPPORTED, "the key/value rows of one head span 2 GiB or more");
+  }
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(CHAIN_ERR_UNSUPPORTED, "scale must be positive and finite");
   if (overlap(*O, *Q) || overlap(*O, *K) || overlap(*O, *V) || overlap(*L, *Q) || overlap(*L, *K) ||

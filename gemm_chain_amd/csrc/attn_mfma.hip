@@ -18,15 +18,16 @@
 // holds keys {4h..4h+3, 8+4h..8+4h+3}, and the V^T operand is read in that
 // order from the row-major V tile with ds_read_b64_tr_b16.
 //
-// Eight waves per workgroup (two per SIMD) share each staged 64-key K/V tile;
-// tiles are double-buffered in LDS, and the global loads run two tiles ahead
-// (two register sets: tile i+2 is fetched while tile i is computed and tile
-// i+1, fetched one step earlier, is written to the free LDS buffer).  LDS pitches are chosen for conflict-free 16-byte
-// K reads (D+8) and conflict-free transposing V reads (D+32).  Inside each MFMA
-// run the LDS fragments are read kAhead MFMAs ahead of use (pinned with
-// scheduling barriers) and the wave raises its issue priority, so the other
-// wave on the SIMD fills the VALU (softmax) while this one feeds the matrix
-// core.  The reference max is raised only when a row's max grows past it by
+// Eight waves per workgroup (two per SIMD) share each staged 64-key K/V tile.
+// Tiles reach LDS by buffer loads that write LDS directly (64 lanes x 16 bytes
+// per wave-level load, no staging registers, no LDS write instructions) into a
+// ring of four stages fetched three tiles ahead; one barrier per tile.  Staged
+// rows are not padded: 16-byte chunks are XOR-swizzled per row so that the
+// 16-byte K fragment reads and the transposing V reads each hit distinct bank
+// groups.  Inside each MFMA run the LDS fragments are read kAhead MFMAs ahead
+// of use (pinned with scheduling barriers) and the wave raises its issue
+// priority, so the other wave on the SIMD fills the VALU (softmax) while this
+// one feeds the matrix core.  The reference max is raised only when a row's max grows past it by
 // more than 2^8 (exact: O and l share the reference), so the O rescale is rare.
 // The row sum l adds the unrounded f32 probabilities, so the LSE stays exact to
 // f32 rounding whatever chunk order the tiles are visited in.
@@ -39,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;          // keys per tile
 constexpr float kTau = 8.0f;    // lazy rescale threshold (base-2 exponent)
@@ -65,22 +67,32 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 template <int D, int NW, int WH>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
-void attn_mfma_bf16_kernel(const AttnParams p) {
+__device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   constexpr int WQ = NW / WH;               // 32-row query blocks per head
   constexpr int ROWS = 32 * WQ;             // query positions per tile
   constexpr int KS = D / 16;                // k-steps of K.Q^T
   constexpr int DB = D / 32;                // 32-wide blocks of O^T
-  constexpr int LDK = D + 8;                // K pitch: conflict-free 16-byte reads
-  constexpr int LDV = D + 32;               // V pitch: conflict-free transposing reads
-  constexpr int CPR = D / 8;                // 16-byte chunks per key row
-  constexpr int LOADS = BN * CPR / (NW * 64);
-  constexpr int BUF = BN * (LDK + LDV);
-  static_assert(LOADS * NW * 64 == BN * CPR, "tile must split evenly over the workgroup");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+  constexpr int RB = 2 * D;                 // bytes per key row of a staged tile
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;             // rows per 1 KB wave load
+  constexpr int TB = BN * RB;               // bytes of one staged K or V tile
+  constexpr int SB = 2 * TB;                // a stage: the K tile, then the V tile
+  constexpr int NST = 4;                    // stages in the ring
+  constexpr int LPW = BN / RPL / NW;        // 1 KB loads per wave, operand and tile
+  constexpr int LT = 2 * LPW;               // per tile
+  static_assert(LPW * RPL * NW == BN, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char lds[NST * SB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
 
   // ---- work item: (batch, head group, pair of query tiles t and T-1-t)
@@ -100,6 +112,41 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
   const __bf16 *kbase = (const __bf16 *)p.k + b * p.k_sb + kvh * p.k_sh;
   const __bf16 *vbase = (const __bf16 *)p.v + b * p.v_sb + kvh * p.v_sh;
   const float c = p.scale_log2;
+  // Buffer descriptors over this head's K and V rows (byte offsets fit 32 bits:
+  // the host checks that a head's rows span less than 2^31 bytes).
+  const uint32_t kss2 = (uint32_t)p.k_ss * 2u, vss2 = (uint32_t)p.v_ss * 2u;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)kbase, 0, (int)((uint32_t)(p.Sk - 1) * kss2 + 2 * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)vbase, 0, (int)((uint32_t)(p.Sk - 1) * vss2 + 2 * D), 0x00020000);
+
+  // Rows of a staged tile are not padded: 16-byte chunk c of key row r sits at
+  // chunk c ^ kswz(r) in K and c ^ vswz(r) in V.  kswz spreads the 16-byte
+  // fragment reads of 16 consecutive keys over 16 distinct bank groups; vswz
+  // does the same for the 4 rows x 4 chunks a transposing read touches per
+  // 32 lanes.  The load side picks which global chunk each lane fetches, so the
+  // swizzle costs nothing there.
+  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  int lrow[LPW], kch[LPW], vch[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    lrow[q] = (wave * LPW + q) * RPL + lane / CPR;
+    kch[q] = (lane % CPR) ^ kswz(lrow[q]);
+    vch[q] = (lane % CPR) ^ vswz(lrow[q]);
+  }
+  // Per-lane byte offsets of the MFMA fragments within a stage.
+  int koff[KS], voff[DB];
+  {
+    const int xk = kswz(l32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = l32 * RB + (((2 * ks + h2) ^ xk) << 4);
+    const int trow = 4 * h2 + ((lane & 15) >> 2);
+    const int ylane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int xv = D == 128 ? (trow & 3) : ((trow >> 1) & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) voff[db] = TB + trow * RB + ((4 * (db ^ xv) + ylane) << 4) + 8 * (lane & 1);
+  }
 
   for (int pass = 0; pass < 2; ++pass) {
     const int t = pass == 0 ? pr : T - 1 - pr;
@@ -142,60 +189,57 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
         if (range_live(ri)) { k0 = p.kr.beg[ri]; return true; }
       return false;
     };
-    struct Tl { int ri, k0; bool valid; };
+    struct Tl { int ri, k0, kend, off; bool valid; };   // range end and position offset cached
     auto first_tile = [&]() -> Tl {
       for (int r = 0; r < p.kr.n; ++r)
-        if (range_live(r)) return Tl{r, p.kr.beg[r], true};
-      return Tl{0, 0, false};
+        if (range_live(r)) return Tl{r, p.kr.beg[r], p.kr.end[r], p.kr.pos_off[r], true};
+      return Tl{0, 0, 0, 0, false};
     };
     auto next_tile = [&](Tl x) -> Tl {
       if (!x.valid) return x;
       int r = x.ri, k = x.k0;
-      return advance(r, k) ? Tl{r, k, true} : Tl{0, 0, false};
+      return advance(r, k) ? Tl{r, k, p.kr.end[r], p.kr.pos_off[r], true} : Tl{0, 0, 0, 0, false};
     };
-    // global loads run two tiles ahead: tile j+2 is fetched into one register
-    // set while the set holding tile j+1 is written to LDS after tile j
-    uint4 kA[LOADS], vA[LOADS], kB[LOADS], vB[LOADS];
-    auto gload2 = [&](uint4 (&kr)[LOADS], uint4 (&vr)[LOADS], const Tl &x) {
-      const int kend = p.kr.end[x.ri];
+    // Direct-to-LDS loads of one tile into stage st: each wave-level load puts
+    // 64 lanes x 16 bytes (RPL key rows) into LDS.  Keys past the range end
+    // read its last key; zero_tail clears them once they have landed.
+    auto issue = [&](const Tl &x, int st) {
+      char *sb = lds + st * SB;
+      const int kend = x.kend;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int cidx = tid + i * NW * 64;
-        const int r = cidx / CPR, c8 = cidx % CPR;
-        const int key = x.k0 + r;
-        if (key < kend) {
-          kr[i] = *(const uint4 *)(kbase + (int64_t)key * p.k_ss + c8 * 8);
-          vr[i] = *(const uint4 *)(vbase + (int64_t)key * p.v_ss + c8 * 8);
-        } else {
-          kr[i] = make_uint4(0, 0, 0, 0);
-          vr[i] = make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < LPW; ++q) {
+        const uint32_t key = (uint32_t)min(x.k0 + lrow[q], kend - 1);
+        char *dst = sb + (wave * LPW + q) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)dst, 16,
+                                                 key * kss2 + 16 * kch[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void *)(dst + TB), 16,
+                                                 key * vss2 + 16 * vch[q], 0, 0, 0);
+      }
+    };
+    auto zero_tail = [&](const Tl &x, int st) {
+      const int kend = x.kend;
+      char *sb = lds + st * SB + lane * 16;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < LPW; ++q)
+        if (x.k0 + lrow[q] >= kend) {
+          *(u32x4 *)(sb + (wave * LPW + q) * 1024) = z;
+          *(u32x4 *)(sb + TB + (wave * LPW + q) * 1024) = z;
         }
-      }
     };
-    auto swrite2 = [&](const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS], int buf) {
-      __bf16 *ks = smem + buf * BUF;
-      __bf16 *vs = ks + BN * LDK;
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int cidx = tid + i * NW * 64;
-        const int r = cidx / CPR, c8 = cidx % CPR;
-        *(uint4 *)(ks + r * LDK + c8 * 8) = kr[i];
-        *(uint4 *)(vs + r * LDV + c8 * 8) = vr[i];
-      }
-    };
-    auto compute = [&](const int ri, const int k0, const int buf) {
+    auto compute = [&](const Tl &x, const int st) {
+      const int k0 = x.k0;
       // ---- compute on the staged tile
-      const int off = p.kr.pos_off[ri];
-      const int nvalid = min(BN, p.kr.end[ri] - k0);
+      const int off = x.off;
+      const int nvalid = min(BN, x.kend - k0);
       const int cls = classify_tile(p.causal, w_qmin, w_qmax, k0 + off, k0 + nvalid - 1 + off, nvalid < BN);
       if (wave_rows && cls != TILE_SKIP) {
-        const __bf16 *ks = smem + buf * BUF;
-        const __bf16 *vs = ks + BN * LDK;
+        const char *sb = lds + st * SB;
         f32x16 s[2] = {f32x16{}, f32x16{}};
         __builtin_amdgcn_s_setprio(1);
         {
           constexpr int N = 2 * KS;
-          auto addr = [&](int i) { return ks + ((i & 1) * 32 + l32) * LDK + (i >> 1) * 16 + 8 * h2; };
+          auto addr = [&](int i) { return sb + koff[i >> 1] + (i & 1) * 32 * RB; };
           bf16x8 kf[kAhead];
 #pragma unroll
           for (int i = 0; i < kAhead; ++i) kf[i] = *(const bf16x8 *)addr(i);
@@ -251,27 +295,25 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
           }
         l += rs;
         // O^T += V^T . P^T
-        const int trow = 4 * h2 + ((lane & 15) >> 2);
-        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         __builtin_amdgcn_s_setprio(1);
         {
           constexpr int N = 4 * DB;
           auto addr = [&](int i) {
             const int db = i >> 2, kb = (i >> 1) & 1, hh = i & 1;
-            return vs + (kb * 32 + 16 * hh + trow) * LDV + db * 32 + tcol;
+            return (const __bf16 *)(sb + voff[db] + (kb * 32 + 16 * hh) * RB);
           };
           i16x4 vlo[kAhead], vhi[kAhead];
 #pragma unroll
           for (int i = 0; i < kAhead; ++i) {
             vlo[i] = ds_read_tr(addr(i));
-            vhi[i] = ds_read_tr(addr(i) + 8 * LDV);
+            vhi[i] = ds_read_tr(addr(i) + 8 * D);
           }
 #pragma unroll
           for (int i = 0; i < N; ++i) {
             const i16x8 a16 = __builtin_shufflevector(vlo[i % kAhead], vhi[i % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
             if (i + kAhead < N) {
               vlo[i % kAhead] = ds_read_tr(addr(i + kAhead));
-              vhi[i % kAhead] = ds_read_tr(addr(i + kAhead) + 8 * LDV);
+              vhi[i % kAhead] = ds_read_tr(addr(i + kAhead) + 8 * D);
             }
             acc[i >> 2] = mfma32(__builtin_bit_cast(bf16x8, a16), pk[(i >> 1) & 1][i & 1], acc[i >> 2]);
         __builtin_amdgcn_sched_barrier(0);
@@ -281,31 +323,36 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
       __builtin_amdgcn_s_setprio(0);
     };
 
-    Tl w0 = first_tile(), w1 = next_tile(w0), w2 = next_tile(w1);
+    // Ring of NST stages (tile j in stage j % NST), fetched three tiles ahead.
+    // Past the last tile the free stage is refilled with the current tile, so
+    // every step has the same number of loads in flight.  Stage j+3 reuses the
+    // buffer of tile j-1, whose reads finished before the previous barrier.
+    Tl w0 = first_tile(), w1 = next_tile(w0), w2 = next_tile(w1), w3 = next_tile(w2);
     if (w0.valid) {
-      gload2(kA, vA, w0);
-      swrite2(kA, vA, 0);
+      issue(w0, 0);
+      issue(w1.valid ? w1 : w0, 1);
+      issue(w2.valid ? w2 : w0, 2);
+      wait_vmcnt<2 * LT>();
+      if (w0.k0 + BN > w0.kend) zero_tail(w0, 0);
     }
-    if (w1.valid) gload2(kB, vB, w1);
-    __syncthreads();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
     int j = 0;
-    // x: register set holding w1 (written to LDS after this tile); y: set for w2
-    auto step = [&](uint4 (&kx)[LOADS], uint4 (&vx)[LOADS], uint4 (&ky)[LOADS], uint4 (&vy)[LOADS]) {
-      const int buf = j & 1;
-      if (w2.valid) gload2(ky, vy, w2);
-      compute(w0.ri, w0.k0, buf);
-      if (w1.valid) swrite2(kx, vx, buf ^ 1);
-      __syncthreads();
+    while (w0.valid) {
+      issue(w3.valid ? w3 : w0, (j + 3) % NST);
+      compute(w0, j % NST);
+      wait_vmcnt<2 * LT>();   // this wave's part of tile j+1 has landed
+      if (w1.valid && w1.k0 + BN > w1.kend) zero_tail(w1, (j + 1) % NST);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
       w0 = w1;
       w1 = w2;
-      w2 = next_tile(w2);
+      w2 = w3;
+      w3 = next_tile(w3);
       ++j;
-    };
-    while (w0.valid) {
-      step(kB, vB, kA, vA);
-      if (!w0.valid) break;
-      step(kA, vA, kB, vB);
     }
+    wait_vmcnt<0>();   // no load into LDS may outlive the pass
+    __builtin_amdgcn_s_barrier();
 
     // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
     const float lt = pair_sum(l);
@@ -334,21 +381,37 @@ void attn_mfma_bf16_kernel(const AttnParams p) {
   }
 }
 
-template <int D, int NW, int WH>
-hipError_t launch(const AttnParams &p, hipStream_t s) {
-  constexpr int ROWS = 32 * (NW / WH);
-  const int T = (p.Sq + ROWS - 1) / ROWS;
-  const int items = p.B * (p.Hq / WH) * ((T + 1) / 2);
-  hipLaunchKernelGGL((attn_mfma_bf16_kernel<D, NW, WH>), dim3(items), dim3(NW * 64), 0, s, p);
-  return hipGetLastError();
-}
+// One plain kernel per configuration (the body is a template).
+#define CHAIN_ATTN_KERNEL(D, WH)                                                               \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
+  void attn_mfma_bf16_kernel_d##D##_g##WH(const AttnParams p) { attn_mfma_bf16<D, 8, WH>(p); }
+CHAIN_ATTN_KERNEL(64, 1)
+CHAIN_ATTN_KERNEL(64, 2)
+CHAIN_ATTN_KERNEL(64, 4)
+CHAIN_ATTN_KERNEL(128, 1)
+CHAIN_ATTN_KERNEL(128, 2)
+CHAIN_ATTN_KERNEL(128, 4)
+#undef CHAIN_ATTN_KERNEL
 
+// Workgroups: pairs of 64-row query tiles of WH query heads (8 waves of 32 rows).
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const int group = p.Hq / p.Hkv;
-  if (group % 4 == 0) return launch<D, 8, 4>(p, s);
-  if (group % 2 == 0) return launch<D, 8, 2>(p, s);
-  return launch<D, 8, 1>(p, s);
+  const int wh = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  const int rows = 32 * (8 / wh);
+  const int T = (p.Sq + rows - 1) / rows;
+  const int items = p.B * (p.Hq / wh) * ((T + 1) / 2);
+  const dim3 grid(items), block(512);
+  if (D == 64) {
+    if (wh == 4) hipLaunchKernelGGL(attn_mfma_bf16_kernel_d64_g4, grid, block, 0, s, p);
+    else if (wh == 2) hipLaunchKernelGGL(attn_mfma_bf16_kernel_d64_g2, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(attn_mfma_bf16_kernel_d64_g1, grid, block, 0, s, p);
+  } else {
+    if (wh == 4) hipLaunchKernelGGL(attn_mfma_bf16_kernel_d128_g4, grid, block, 0, s, p);
+    else if (wh == 2) hipLaunchKernelGGL(attn_mfma_bf16_kernel_d128_g2, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(attn_mfma_bf16_kernel_d128_g1, grid, block, 0, s, p);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -79,6 +79,19 @@ def _valid(B=1, Hq=4, Hkv=2, S=256, D=64, dt=chain.BF16, odt=None):
 CODES = {n: i for i, n in enumerate(chain.STATUS)}
 
 
+def test_attn_rows_of_a_head_must_span_under_2gib(lib):
+    """bf16 kernels address a head's key/value rows with 32-bit byte offsets."""
+    Q, K, V, O, L = _valid()
+    far = FAKE + 2 ** 44
+    for stride_s, ok in ((2 ** 22, True), (2 ** 23, False)):
+        Kw = td([1, 2, 256, 64], chain.BF16, far, stride=[2 ** 40, 2 ** 31, stride_s, 1])
+        Vw = td([1, 2, 256, 64], chain.BF16, far + 2 ** 42, stride=[2 ** 40, 2 ** 31, stride_s, 1])
+        rc = _attn(lib, Q, Kw, Vw, O, L, scale=-1.0)   # a valid span fails later, at the scale check
+        assert rc == CODES["CHAIN_ERR_UNSUPPORTED"]
+        msg = lib.chain_last_error().decode()
+        assert ("2 GiB" in msg) != ok, (stride_s, msg)
+
+
 def test_attn_validation_codes(lib):
     Q, K, V, O, L = _valid()
     P = ctypes.byref
