@@ -14,15 +14,16 @@
 // of v_mfma_f32_32x32x16_bf16 blocks whose f32 accumulators live in AGPRs.
 // Operands are swapped in the MFMA (it computes the transposed block) so a lane
 // ends up holding four consecutive output columns of one row: 8-byte stores.
-// A and B k-tiles of 64 are staged in LDS (two buffers) through registers; the
-// global fetch of tile k+2 is issued right after tile k+1 is written to LDS, so
-// it has most of a k-tile of MFMA work to arrive.  Within a tile the fragments
-// of k-step s+1 are read while the MFMAs of step s issue.  A (and a k-major B)
-// sits in LDS as [rows][64 + 8] (16-byte fragment reads hit distinct banks);
-// an n-major B sits as [64][BN' + 32] and is read with ds_read_b64_tr_b16.
-// Tiles that reach past M, N or K take a guarded load path (clamped address,
-// zero fill); all others take plain loads.  The f32 path for f32 inputs keeps
-// a 128 x 128 x 32 tile per 256 threads with v_mfma_f32_32x32x2_f32.
+// Two ways of feeding LDS, by weight layout:
+//  - k-contiguous B (gemm_bf16_dtl_kernel_NBW): loads that write LDS directly
+//    fill a ring of four k-stages of 32, fetched three stages ahead, rows
+//    XOR-swizzled instead of padded;
+//  - n-contiguous B (gemm_bf16_kernel<NBW>): k-tiles of 64 staged through
+//    registers into two LDS buffers; A as [256][64 + 8], B as [64][BN' + 32]
+//    read with ds_read_b64_tr_b16.
+// Both give the same MFMA operands in the same k order.  The f32 path for f32
+// inputs keeps a 128 x 128 x 32 tile per 256 threads with
+// v_mfma_f32_32x32x2_f32.
 #include "internal.h"
 
 #include <type_traits>
@@ -58,16 +59,17 @@ constexpr int LDA = BK + 8;        // pitch of k-contiguous stages
 
 __device__ inline u32x4 ld16(const __bf16 *p) { return *(const u32x4 *)p; }
 
-// NBW = 32-column blocks per wave (BN = 64 * NBW); KMAJ: B has k contiguous.
-template <int NBW, bool KMAJ>
+// n-contiguous B (row-major [K, N] weights).  NBW = 32-column blocks per wave
+// (BN = 64 * NBW).
+template <int NBW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const GemmParams p) {
   constexpr int BN = 64 * NBW, WTN = 32 * NBW;
-  constexpr int LDBN = ((BN + 127) / 128) * 128 + 32;   // n-major pitch: conflict-free tr reads
-  constexpr int BSZ = KMAJ ? BN * LDA : BK * LDBN;
+  constexpr int LDBN = ((BN + 127) / 128) * 128 + 32;   // B pitch: conflict-free tr reads
+  constexpr int BSZ = BK * LDBN;
   constexpr int AL = BM * BK / 8 / 256;                  // 16-byte chunks per thread
   constexpr int BL = BN * BK / 8 / 256;
-  constexpr int BCH = BN / 8;                            // chunks per n-major B row
+  constexpr int BCH = BN / 8;                            // chunks per B row
   __shared__ __attribute__((aligned(16))) __bf16 as[2][BM * LDA];
   __shared__ __attribute__((aligned(16))) __bf16 bs[2][BSZ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -80,17 +82,16 @@ void gemm_bf16_kernel(const GemmParams p) {
   const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
   const __bf16 *A = (const __bf16 *)p.a;
   const __bf16 *B = (const __bf16 *)p.b;
-  const int64_t ldb = KMAJ ? p.b_sn : p.b_sk;
+  const int64_t ldb = p.b_sk;
   const int nk = (p.K + BK - 1) / BK;
   const int nk_plain = (m0 + BM <= p.M && n0 + BN <= p.N) ? p.K / BK : 0;
 
   // Chunk c = tid + 256 i of a stage: A row (c >> 3) = (tid >> 3) + 32 i, k
-  // chunk c & 7 = tid & 7; likewise for a k-major B.  An n-major B row holds
-  // BCH chunks.  Per-thread byte offsets stay 32-bit; the per-i part is uniform.
+  // chunk c & 7 = tid & 7; a B row holds BCH chunks.  Per-thread byte offsets
+  // stay 32-bit; the per-i part is uniform.
   const char *Ab = (const char *)A, *Bb = (const char *)B;
   const uint32_t a_off = (uint32_t)((tid >> 3) * p.lda + (tid & 7) * 8) * 2u;
-  const uint32_t b_off = KMAJ ? (uint32_t)((tid >> 3) * ldb + (tid & 7) * 8) * 2u
-                              : (uint32_t)((tid / BCH) * ldb + (tid % BCH) * 8) * 2u;
+  const uint32_t b_off = (uint32_t)((tid / BCH) * ldb + (tid % BCH) * 8) * 2u;
   u32x4 ar[AL], br[BL];
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
@@ -103,10 +104,7 @@ void gemm_bf16_kernel(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < BL; ++i) {
         const int c = tid + 256 * i;
-        if (KMAJ) {
-          const char *base = Bb + ((int64_t)(n0 + 32 * i) * ldb + k0) * 2;
-          br[i] = *(const u32x4 *)(base + b_off);
-        } else if (256 % BCH == 0) {
+        if (256 % BCH == 0) {
           const char *base = Bb + ((int64_t)(k0 + (256 / BCH) * i) * ldb + n0) * 2;
           br[i] = *(const u32x4 *)(base + b_off);
         } else {
@@ -126,11 +124,9 @@ void gemm_bf16_kernel(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < BL; ++i) {
         const int c = tid + 256 * i;
-        int gk, gn;
-        if (KMAJ) gn = n0 + (c >> 3), gk = k0 + (c & 7) * 8;
-        else gk = k0 + c / BCH, gn = n0 + (c % BCH) * 8;
+        const int gk = k0 + c / BCH, gn = n0 + (c % BCH) * 8;
         const bool ok = gk < p.K && gn < p.N;
-        const u32x4 v = ld16(ok ? (KMAJ ? B + (int64_t)gn * ldb + gk : B + (int64_t)gk * ldb + gn) : B);
+        const u32x4 v = ld16(ok ? B + (int64_t)gk * ldb + gn : B);
         br[i] = ok ? v : z;
       }
     }
@@ -144,8 +140,7 @@ void gemm_bf16_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       const int c = tid + 256 * i;
-      if (KMAJ) *(u32x4 *)(&bs[buf][(c >> 3) * LDA + (c & 7) * 8]) = br[i];
-      else *(u32x4 *)(&bs[buf][(c / BCH) * LDBN + (c % BCH) * 8]) = br[i];
+      *(u32x4 *)(&bs[buf][(c / BCH) * LDBN + (c % BCH) * 8]) = br[i];
     }
   };
 
@@ -160,14 +155,10 @@ void gemm_bf16_kernel(const GemmParams p) {
       f.a[i] = *(const bf16x8 *)(&as[buf][(wm * 128 + i * 32 + l32) * LDA + ks * 16 + 8 * h2]);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      if (KMAJ) {
-        f.b[j] = *(const bf16x8 *)(&bs[buf][(wn * WTN + j * 32 + l32) * LDA + ks * 16 + 8 * h2]);
-      } else {
-        const __bf16 *src = &bs[buf][(ks * 16 + 8 * h2 + trow) * LDBN + wn * WTN + j * 32 + tcol];
-        const i16x4 lo = ds_read_tr(src);
-        const i16x4 hi = ds_read_tr(src + 4 * LDBN);
-        f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+      const __bf16 *src = &bs[buf][(ks * 16 + 8 * h2 + trow) * LDBN + wn * WTN + j * 32 + tcol];
+      const i16x4 lo = ds_read_tr(src);
+      const i16x4 hi = ds_read_tr(src + 4 * LDBN);
+      f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
 
@@ -523,17 +514,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
     }
 }
 
-template <int NBW, bool KMAJ>
+template <int NBW>
 void launch_bf16(const GemmParams &p, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * NBW - 1) / (64 * NBW));
-  hipLaunchKernelGGL((gemm_bf16_kernel<NBW, KMAJ>), dim3(tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<NBW>), dim3(tiles), dim3(256), 0, stream, p);
 }
 
-template <bool KMAJ>
 void launch_bf16_width(const GemmParams &p, int nbw, hipStream_t stream) {
-  if (nbw == 4) launch_bf16<4, KMAJ>(p, stream);
-  else if (nbw == 3) launch_bf16<3, KMAJ>(p, stream);
-  else launch_bf16<2, KMAJ>(p, stream);
+  if (nbw == 4) launch_bf16<4>(p, stream);
+  else if (nbw == 3) launch_bf16<3>(p, stream);
+  else launch_bf16<2>(p, stream);
 }
 
 void launch_dtl(const GemmParams &p, int nbw, hipStream_t stream) {
@@ -577,7 +567,7 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
     if (p.b_sk == 1) {
       launch_dtl(p, nbw, stream);
     } else {
-      launch_bf16_width<false>(p, nbw, stream);
+      launch_bf16_width(p, nbw, stream);
     }
   } else {
     const int tiles = ((p.M + TM - 1) / TM) * ((p.N + TN - 1) / TN);
