@@ -45,8 +45,24 @@ __device__ inline i16x4 ds_read_tr(const __bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26 (after Hastings): erf(x) = 1 - t (a1 + a2 t + ... + a5 t^4) exp(-x^2),
+// t = 1 / (1 + p x) for x >= 0, odd in x; absolute error at most 1.5e-7.  One
+// reciprocal and one exp2 instead of a general-purpose erff, which matters in
+// an epilogue no other wave can overlap.
+__device__ inline float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * ax * ax);
+  return copysignf(fmaf(-q * t, e, 1.f), x);
+}
+
 __device__ inline float activate(float z, int act) {
-  if (act == CHAIN_ACT_GELU_ERF) return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+  if (act == CHAIN_ACT_GELU_ERF) return 0.5f * z * (1.f + erf_as(z * 0.70710678118654752f));
   if (act == CHAIN_ACT_GELU_TANH) {
     const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
     return 0.5f * z * (1.f + tanhf(u));
