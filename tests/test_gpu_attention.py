@@ -292,3 +292,19 @@ def test_merge_part_counts_against_oracle(C, D):
     assert max_abs(f64(ml), rl) <= 1e-5
     mb, _ = chain.lse_merge(o.to(dev), lse.to(dev), out_dtype=torch.bfloat16)
     assert max_abs(f64(mb), ro) <= 2e-2
+
+
+@pytest.mark.parametrize("D,n_chunks,zigzag", [(128, 5, True), (64, 1, False)])
+def test_strided_kv_views_match_contiguous(D, n_chunks, zigzag):
+    """K and V as head-major views ([B, S, H, D] storage): same bits as contiguous inputs."""
+    dev = device()
+    q, k, v = gen_attention(2, 8, 2, 320, 320, D, "bf16", 1.0, 23)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ks = k.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+    vs = v.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+    assert ks.stride(2) == 2 * D and vs.stride(2) == 2 * D
+    announce(f"strided K/V D{D} chunks {n_chunks} zigzag {zigzag}")
+    o1, l1 = chain.attn_fwd(qd, ks, vs, causal=True, n_chunks=n_chunks, zigzag=zigzag)
+    o2, l2 = chain.attn_fwd(qd, kd, vd, causal=True, n_chunks=n_chunks, zigzag=zigzag)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
