@@ -44,6 +44,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;          // keys per tile
 constexpr float kTau = 8.0f;    // lazy rescale threshold (base-2 exponent)
+constexpr float kLaneSumMax = 256.0f;   // 2^kTau
 constexpr int kAhead = 4;       // LDS fragments in flight ahead of their MFMA
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -266,33 +267,53 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
               s[kb][r] = kr <= lim ? s[kb][r] : -INFINITY;
             }
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        // the reference max is raised only when the row max exceeds it by more
-        // than 2^kTau (exact: O and l share the reference); the O rescale is rare
-        const float tmax = pair_max(mx) * c;
-        if (__any(tmax > m + kTau)) {
-          const float m_new = fmaxf(m, tmax);
-          const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
-          m = m_new;
-          l *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        }
-        const float m_use = m == -INFINITY ? 0.f : m;
+        // Fast path: probabilities against the current reference.  The row max
+        // only decides whether the reference must rise (a term above 2^kTau); a
+        // lane sum of at most 2^kTau proves no term is, so the max is computed
+        // (and the rule below applied) only when some lane sum exceeds it, or
+        // before the first reference exists.
         float rs = 0.f;
         bf16x8 pk[2][2];
+        bool slow = __any(m == -INFINITY);
+        if (!slow) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
-            rs += e;
-            pk[kb][r >> 3][r & 7] = (__bf16)e;
+            for (int r = 0; r < 16; ++r) {
+              const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m));
+              rs += e;
+              pk[kb][r >> 3][r & 7] = (__bf16)e;
+            }
+          slow = __any(!(rs <= kLaneSumMax));
+        }
+        if (slow) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+          // the reference max is raised only when the row max exceeds it by more
+          // than 2^kTau (exact: O and l share the reference); the O rescale is rare
+          const float tmax = pair_max(mx) * c;
+          if (__any(tmax > m + kTau)) {
+            const float m_new = fmaxf(m, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
           }
+          const float m_use = m == -INFINITY ? 0.f : m;
+          rs = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
+              rs += e;
+              pk[kb][r >> 3][r & 7] = (__bf16)e;
+            }
+        }
         l += rs;
         // O^T += V^T . P^T
         __builtin_amdgcn_s_setprio(1);
