@@ -136,7 +136,9 @@ const char *chain_last_error(void);
  *            of S into 2*n_chunks equal pieces (TSP article, zigzag partition);
  *            zero: chunk s is the s-th of n_chunks contiguous ranges
  * The result does not depend on n_chunks/zigzag beyond floating-point
- * rounding.  D must be 64 or 128 (CHAIN_ERR_UNSUPPORTED otherwise).
+ * rounding.  D must be 64 or 128, and for bf16 the key (and the value) rows
+ * of one head must span less than 2^31 bytes, i.e. ((S - 1) * stride + D) * 2
+ * < 2^31 (CHAIN_ERR_UNSUPPORTED otherwise).
  */
 chain_status chain_attn_fwd(const chain_tensor *Q, const chain_tensor *K,
                             const chain_tensor *V, const chain_tensor *O,
@@ -156,7 +158,8 @@ chain_status chain_attn_fwd(const chain_tensor *Q, const chain_tensor *K,
  *   q_pos, kv_pos  host chain_segs covering exactly Sq and Sk rows
  * With causal, key j is visible to query i iff kv_pos(j) <= q_pos(i).  A row
  * that sees no key gets O_part = 0 and LSE_part = -inf (never NaN).
- * Sk == 0 is valid (every row is then such a row).  D must be 64 or 128.
+ * Sk == 0 is valid (every row is then such a row).  D must be 64 or 128; the
+ * 2^31-byte limit on one head's key/value rows applies as for chain_attn_fwd.
  */
 chain_status chain_attn_partial(const chain_tensor *Q, const chain_tensor *Kc,
                                 const chain_tensor *Vc, const chain_tensor *O_part,
