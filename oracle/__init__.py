@@ -22,6 +22,7 @@ Sources (cited by page and section; the text of the pages is not quoted):
 
 Modules:
   attention -- softmax(scale.Q.K^T + causal mask).V with per-row log-sum-exp
+  attention_bwd -- its gradients dQ, dK, dV for an output gradient dO
   merge     -- combination of partial (O, LSE) results
   mlp       -- act(X.W1).W2 with erf-GeLU, tanh-GeLU or identity
   zigzag    -- zigzag shares and chunks of a sequence; visible-pair counts
@@ -34,13 +35,14 @@ exact float64); that detail is covered only by the tolerance.
 """
 
 from .attention import attention, attention_rows, visible_mask
+from .attention_bwd import attention_bwd, attention_bwd_loss
 from .merge import lse_merge
 from .mlp import gelu_erf, gelu_tanh, mlp, ACTIVATIONS
 from .zigzag import (natural_chunk_positions, zigzag_chunk_positions,
                      zigzag_share_positions, visible_pairs)
 
 __all__ = [
-    "attention", "attention_rows", "visible_mask", "lse_merge", "gelu_erf",
+    "attention", "attention_rows", "visible_mask", "attention_bwd", "attention_bwd_loss", "lse_merge", "gelu_erf",
     "gelu_tanh", "mlp", "ACTIVATIONS", "natural_chunk_positions",
     "zigzag_chunk_positions", "zigzag_share_positions", "visible_pairs",
 ]
