@@ -70,6 +70,8 @@ def load():
         "chain_lse_merge": (ctypes.c_int, [T, T, T, T, vp]),
         "chain_mlp_fwd": (ctypes.c_int, [T, T, T, T, ctypes.c_int, vp, sz, vp]),
         "chain_mlp_workspace_bytes": (sz, [i64, i64, i32]),
+        "chain_attn_bwd": (ctypes.c_int, [T, T, T, T, T, T, T, T, T, ctypes.c_int, f32, vp, sz, vp]),
+        "chain_attn_bwd_workspace_bytes": (sz, [i64, i64, i64]),
         "chain_zigzag_segs": (ctypes.c_int, [i64, i32, i32, S]),
         "chain_attn_tile_census": (ctypes.c_int, [i64, S, i64, S, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -161,6 +163,28 @@ def lse_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=None, 
     _check(lib.chain_lse_merge(desc(o_parts), desc(lse_parts), desc(o),
                                desc(l) if l is not None else None, _stream(o_parts)))
     return o, l
+
+
+def attn_bwd_workspace_bytes(B, Hq, S):
+    return int(load().chain_attn_bwd_workspace_bytes(int(B), int(Hq), int(S)))
+
+
+def attn_bwd(q, k, v, o, lse, do, causal=True, scale=None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """(dQ, dK, dV) in f32 for bf16 attention whose forward gave (O, LSE)."""
+    lib = load()
+    B, Hq, S, D = q.shape
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, Hq, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.chain_attn_bwd(desc(q), desc(k), desc(v), desc(o), desc(lse), desc(do), desc(dq),
+                              desc(dk), desc(dv), int(bool(causal)), _scale(scale, D),
+                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                              _stream(q)))
+    return dq, dk, dv
 
 
 def mlp_workspace_bytes(M, N, dtype=torch.bfloat16):

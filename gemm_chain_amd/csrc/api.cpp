@@ -372,6 +372,83 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
   return ok();
 }
 
+size_t chain_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t S) {
+  if (B < 0 || Hq < 0 || S < 0) return 0;
+  const size_t b = (size_t)B * (size_t)Hq * (size_t)S * 4;
+  return (b + 255) / 256 * 256;
+}
+
+chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const chain_tensor *V,
+                            const chain_tensor *O, const chain_tensor *LSE, const chain_tensor *dO,
+                            const chain_tensor *dQ, const chain_tensor *dK, const chain_tensor *dV,
+                            int causal, float scale, void *workspace, size_t ws_bytes, void *stream) {
+  TRY(check_attn(Q, K, V, O, LSE, scale, false));
+  TRY(check_tensor(dO, "dO", 4));
+  TRY(check_tensor(dQ, "dQ", 4));
+  TRY(check_tensor(dK, "dK", 4));
+  TRY(check_tensor(dV, "dV", 4));
+  if (Q->dtype != CHAIN_BF16 || dO->dtype != CHAIN_BF16)
+    return fail(CHAIN_ERR_DTYPE, "Q, K, V, O and dO must be bf16");
+  if (dQ->dtype != CHAIN_F32 || dK->dtype != CHAIN_F32 || dV->dtype != CHAIN_F32)
+    return fail(CHAIN_ERR_DTYPE, "dQ, dK and dV must be f32");
+  const int64_t B = Q->shape[0], Hq = Q->shape[1], S = Q->shape[2], D = Q->shape[3];
+  if (K->shape[2] != S) return fail(CHAIN_ERR_SHAPE, "the backward needs as many keys as queries");
+  for (int i = 0; i < 4; ++i) {
+    if (dO->shape[i] != Q->shape[i] || dQ->shape[i] != Q->shape[i])
+      return fail(CHAIN_ERR_SHAPE, "dO and dQ must have the shape of Q");
+    if (dK->shape[i] != K->shape[i] || dV->shape[i] != K->shape[i])
+      return fail(CHAIN_ERR_SHAPE, "dK and dV must have the shape of K");
+  }
+  if (B * Hq * S > INT32_MAX) return fail(CHAIN_ERR_UNSUPPORTED, "B * Hq * S beyond 2^31");
+  const chain_tensor *ins[] = {Q, K, V, O, LSE, dO};
+  const chain_tensor *outs[] = {dQ, dK, dV};
+  for (int i = 0; i < 3; ++i) {
+    for (const chain_tensor *t : ins)
+      if (overlap(*outs[i], *t)) return fail(CHAIN_ERR_ALIAS, "outputs overlap inputs or each other");
+    for (int j = 0; j < i; ++j)
+      if (overlap(*outs[i], *outs[j])) return fail(CHAIN_ERR_ALIAS, "outputs overlap inputs or each other");
+  }
+  const size_t need = chain_attn_bwd_workspace_bytes(B, Hq, S);
+  if (B == 0 || Hq == 0 || S == 0) return ok();
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(CHAIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if ((uintptr_t)workspace % 256) return fail(CHAIN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  {
+    chain_tensor W{};
+    W.data = workspace;
+    W.dtype = CHAIN_F32;
+    W.ndim = 1;
+    W.shape[0] = B * Hq * S;
+    W.stride[0] = 1;
+    for (const chain_tensor *t : ins)
+      if (overlap(W, *t)) return fail(CHAIN_ERR_ALIAS, "workspace overlaps a tensor");
+    for (const chain_tensor *t : outs)
+      if (overlap(W, *t)) return fail(CHAIN_ERR_ALIAS, "workspace overlaps a tensor");
+  }
+  chain::AttnBwdParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = Q->data, p.k = K->data, p.v = V->data, p.o = O->data, p.dout = dO->data;
+  p.lse = (const float *)LSE->data;
+  p.dq = (float *)dQ->data, p.dk = (float *)dK->data, p.dv = (float *)dV->data;
+  p.drow = (float *)workspace;
+  p.q_sb = Q->stride[0], p.q_sh = Q->stride[1], p.q_ss = Q->stride[2];
+  p.k_sb = K->stride[0], p.k_sh = K->stride[1], p.k_ss = K->stride[2];
+  p.v_sb = V->stride[0], p.v_sh = V->stride[1], p.v_ss = V->stride[2];
+  p.o_sb = O->stride[0], p.o_sh = O->stride[1], p.o_ss = O->stride[2];
+  p.do_sb = dO->stride[0], p.do_sh = dO->stride[1], p.do_ss = dO->stride[2];
+  p.l_sb = LSE->stride[0], p.l_sh = LSE->stride[1], p.l_ss = LSE->stride[2];
+  p.dq_sb = dQ->stride[0], p.dq_sh = dQ->stride[1], p.dq_ss = dQ->stride[2];
+  p.dk_sb = dK->stride[0], p.dk_sh = dK->stride[1], p.dk_ss = dK->stride[2];
+  p.dv_sb = dV->stride[0], p.dv_sh = dV->stride[1], p.dv_ss = dV->stride[2];
+  p.B = (int32_t)B, p.Hq = (int32_t)Hq, p.Hkv = (int32_t)K->shape[1], p.S = (int32_t)S;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = chain::launch_attn_bwd(p, (int)D, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CHAIN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 chain_status chain_zigzag_segs(int64_t S, int32_t parts, int32_t r, chain_segs *out) {
   if (out == nullptr) return fail(CHAIN_ERR_NULL, "out is NULL");
   if (parts < 1 || S <= 0 || S % (2 * (int64_t)parts))

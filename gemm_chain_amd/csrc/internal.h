@@ -167,10 +167,31 @@ struct GemmParams {
   int32_t c_vec;      // 1: C rows allow 4-element vector stores (aligned base and ldc)
 };
 
+struct AttnBwdParams {
+  const void *q, *k, *v, *o, *dout;   // bf16
+  const float *lse;                   // natural log, [B, Hq, S]
+  float *dq, *dk, *dv;                // outputs, f32
+  float *drow;                        // workspace: D_i = sum_d dO_id O_id, [B, Hq, S] dense
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t do_sb, do_sh, do_ss;
+  int64_t l_sb, l_sh, l_ss;
+  int64_t dq_sb, dq_sh, dq_ss;
+  int64_t dk_sb, dk_sh, dk_ss;
+  int64_t dv_sb, dv_sh, dv_ss;
+  int32_t B, Hq, Hkv, S;
+  int32_t causal;
+  float scale;        // multiplies Q.K^T
+  float scale_log2;   // scale * log2(e)
+};
+
 // Launchers (defined in the .hip files).  Each returns the launch's hipError_t.
 hipError_t launch_attn_mfma_bf16(const AttnParams &p, int D, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream);
+hipError_t launch_attn_bwd(const AttnBwdParams &p, int D, hipStream_t stream);
 
 }  // namespace chain

@@ -85,6 +85,12 @@ def gen_attention(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", amp=1.0, seed=0):
     return q, k, v
 
 
+def gen_attention_grad(B, Hq, S, D, dtype="bf16", amp=1.0, seed=0):
+    """dO [B,Hq,S,D] on the CPU: the output gradient fed to the attention backward."""
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(B, Hq, S, D, generator=g, dtype=torch.float32) * amp).to(_DTYPES[dtype])
+
+
 def gen_mlp(M, K, N, K2=None, dtype="bf16", amp_x=1.0, amp_w=0.02, seed=0):
     """X [M,K], W1 [K,N], W2 [N,K2] on the CPU, drawn in the order X, W1, W2."""
     K2 = K if K2 is None else K2

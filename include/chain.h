@@ -207,6 +207,45 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1,
 size_t chain_mlp_workspace_bytes(int64_t M, int64_t N, int32_t dt);
 
 /*
+ * chain_attn_bwd -- gradients of chain_attn_fwd's attention (bf16, whole key
+ * context, positions 0..S-1) with respect to Q, K and V.  The pages treat the
+ * chain as the core unit of Transformer training (METP article, abstract) and
+ * keep only what the backward needs, recomputing the rest (2D-Attention
+ * summary, "Estrategias de Entrenamiento Distribuido"); the gradient itself is
+ * the chain rule of the forward definition: with P_ij = exp(scale*s_ij - LSE_i)
+ * on visible keys, D_i = sum_d dO_id O_id and dS = P * (dO.V^T - D),
+ *   dQ = scale * dS.K,   dK = scale * dS^T.Q,   dV = P^T.dO,
+ * dK and dV summed over the query heads that share a key/value head.
+ *
+ *   Q    [B, Hq, S, D]   bf16   (input)
+ *   K, V [B, Hkv, S, D]  bf16   (input), Hq % Hkv == 0, grouping as in chain_attn_fwd
+ *   O    [B, Hq, S, D]   bf16   (input: chain_attn_fwd's output)
+ *   LSE  [B, Hq, S]      f32    (input: chain_attn_fwd's log-sum-exp, natural log)
+ *   dO   [B, Hq, S, D]   bf16   (input: gradient of the loss with respect to O)
+ *   dQ   [B, Hq, S, D]   f32    (output)
+ *   dK,dV [B, Hkv, S, D] f32    (output)
+ *   causal, scale  as given to chain_attn_fwd
+ *   workspace  device buffer of at least chain_attn_bwd_workspace_bytes(B, Hq, S)
+ *              bytes, 256-byte aligned; caller-owned scratch (holds D_i)
+ * P is recomputed from Q, K and LSE, so LSE must be the one the forward
+ * produced for these Q and K.  D must be 64 or 128.  Products are bf16 MFMAs
+ * with f32 accumulation; P and dS are rounded to bf16 as MFMA operands.
+ * Every output element is written exactly once (no atomics), so repeated
+ * calls give identical bits.  dQ, dK, dV and the workspace must not overlap
+ * each other or any input (CHAIN_ERR_ALIAS).  Alignment: 16 bytes for all
+ * tensors except LSE (4).  B * Hq * S must be below 2^31 (UNSUPPORTED).
+ */
+chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const chain_tensor *V,
+                            const chain_tensor *O, const chain_tensor *LSE, const chain_tensor *dO,
+                            const chain_tensor *dQ, const chain_tensor *dK, const chain_tensor *dV,
+                            int causal, float scale, void *workspace, size_t ws_bytes,
+                            void *stream);
+
+/* Bytes of workspace chain_attn_bwd needs, rounded up to 256; 0 for negative
+ * sizes. */
+size_t chain_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t S);
+
+/*
  * chain_zigzag_segs -- host helper: the positions of share r of `parts` in a
  * zigzag split of S tokens (TSP article, zigzag partition): the pieces r and
  * 2*parts-1-r of 2*parts equal pieces, as two runs in ascending order.  Used

@@ -242,3 +242,58 @@ def test_tile_census_ring_share(lib):
         n = S // (2 * P)
         got = chain.tile_census(len(qpos), len(kpos), q_pos=qruns, kv_pos=kruns, block_m=32, block_n=64)
         assert got == _census_from_mask(qpos, [kpos[:n], kpos[n:]], True, 32, 64)
+
+
+def _bwd_set(B=1, Hq=4, Hkv=2, S=256, D=64):
+    G = 2 ** 30
+    Q, K, V, O, L = _valid(B, Hq, Hkv, S, D)
+    dO = td([B, Hq, S, D], chain.BF16, FAKE + 5 * G)
+    dQ = td([B, Hq, S, D], chain.F32, FAKE + 6 * G)
+    dK = td([B, Hkv, S, D], chain.F32, FAKE + 7 * G)
+    dV = td([B, Hkv, S, D], chain.F32, FAKE + 8 * G)
+    return dict(Q=Q, K=K, V=V, O=O, L=L, dO=dO, dQ=dQ, dK=dK, dV=dV), FAKE + 9 * G
+
+
+def _bwd(lib, t, ws, ws_bytes, **over):
+    t = dict(t, **over)
+    P = ctypes.byref
+    return lib.chain_attn_bwd(P(t["Q"]), P(t["K"]), P(t["V"]), P(t["O"]), P(t["L"]), P(t["dO"]),
+                              P(t["dQ"]), P(t["dK"]), P(t["dV"]), 1, 0.125, ws, ws_bytes, None)
+
+
+def test_attn_bwd_validation_codes(lib):
+    t, ws = _bwd_set()
+    need = lib.chain_attn_bwd_workspace_bytes(1, 4, 256)
+    assert need == 4 * 256 * 4
+    assert lib.chain_attn_bwd_workspace_bytes(1, 3, 5) == 256
+    assert lib.chain_attn_bwd_workspace_bytes(-1, 3, 5) == 0
+    G = 2 ** 30
+    # Everything else valid: the missing or short workspace is what fails.
+    assert _bwd(lib, t, None, need) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert _bwd(lib, t, ws, need - 1) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert _bwd(lib, t, ws + 16, need) == CODES["CHAIN_ERR_ALIGN"]
+    assert _bwd(lib, t, FAKE + 5 * G + 256, need) == CODES["CHAIN_ERR_ALIAS"]      # inside dO
+    assert _bwd(lib, t, FAKE + 7 * G + 1024, need) == CODES["CHAIN_ERR_ALIAS"]     # inside dK
+    assert _bwd(lib, t, ws, need, dQ=td([1, 4, 256, 64], chain.BF16, FAKE + 6 * G)) == CODES["CHAIN_ERR_DTYPE"]
+    assert _bwd(lib, t, ws, need, dO=td([1, 4, 256, 64], chain.F32, FAKE + 5 * G)) == CODES["CHAIN_ERR_DTYPE"]
+    f32 = _valid(dt=chain.F32)
+    assert _bwd(lib, t, ws, need, Q=f32[0], K=f32[1], V=f32[2], O=f32[3]) == CODES["CHAIN_ERR_DTYPE"]
+    assert _bwd(lib, t, ws, need, dK=td([1, 2, 255, 64], chain.F32, FAKE + 7 * G)) == CODES["CHAIN_ERR_SHAPE"]
+    assert _bwd(lib, t, ws, need, dO=td([1, 4, 255, 64], chain.BF16, FAKE + 5 * G)) == CODES["CHAIN_ERR_SHAPE"]
+    assert _bwd(lib, t, ws, need, dQ=td([1, 4, 256, 64], chain.F32, FAKE + 2048)) == CODES["CHAIN_ERR_ALIAS"]
+    assert _bwd(lib, t, ws, need, dV=td([1, 2, 256, 64], chain.F32, FAKE + 7 * G + 4096)) == CODES["CHAIN_ERR_ALIAS"]
+    assert _bwd(lib, t, ws, need, dV=td([1, 2, 256, 64], chain.F32, FAKE + 8 * G + 8)) == CODES["CHAIN_ERR_ALIGN"]
+    assert _bwd(lib, t, ws, need, dO=td([1, 4, 256, 64], chain.BF16, FAKE + 5 * G,
+                                        stride=[4 * 256 * 68, 256 * 68, 68, 1])) == CODES["CHAIN_ERR_ALIGN"]
+    # keys must match queries
+    t2, _ = _bwd_set()
+    t2["K"] = td([1, 2, 128, 64], chain.BF16, FAKE + G)
+    t2["V"] = td([1, 2, 128, 64], chain.BF16, FAKE + 2 * G)
+    t2["dK"] = td([1, 2, 128, 64], chain.F32, FAKE + 7 * G)
+    t2["dV"] = td([1, 2, 128, 64], chain.F32, FAKE + 8 * G)
+    assert _bwd(lib, t2, ws, need) == CODES["CHAIN_ERR_SHAPE"]
+    t3, _ = _bwd_set(D=96)
+    assert _bwd(lib, t3, ws, need) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    # Empty sequence: valid, nothing launched.
+    t0, _ = _bwd_set(S=0)
+    assert _bwd(lib, t0, None, 0) == CODES["CHAIN_OK"]
