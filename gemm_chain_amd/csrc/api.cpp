@@ -374,7 +374,7 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
 
 size_t chain_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t S) {
   if (B < 0 || Hq < 0 || S < 0) return 0;
-  const size_t b = (size_t)B * (size_t)Hq * (size_t)S * 4;
+  const size_t b = (size_t)B * (size_t)Hq * (size_t)((S + 63) / 64 * 64) * 8;
   return (b + 255) / 256 * 256;
 }
 
@@ -400,6 +400,9 @@ chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const 
       return fail(CHAIN_ERR_SHAPE, "dK and dV must have the shape of K");
   }
   if (B * Hq * S > INT32_MAX) return fail(CHAIN_ERR_UNSUPPORTED, "B * Hq * S beyond 2^31");
+  // The kernels address one head's query and dO rows with 32-bit byte offsets.
+  if (S > 0 && ((S - 1) * Q->stride[2] + D) * 2 > INT32_MAX || S > 0 && ((S - 1) * dO->stride[2] + D) * 2 > INT32_MAX)
+    return fail(CHAIN_ERR_UNSUPPORTED, "the query or dO rows of one head span 2 GiB or more");
   const chain_tensor *ins[] = {Q, K, V, O, LSE, dO};
   const chain_tensor *outs[] = {dQ, dK, dV};
   for (int i = 0; i < 3; ++i) {
@@ -418,7 +421,7 @@ chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const 
     W.data = workspace;
     W.dtype = CHAIN_F32;
     W.ndim = 1;
-    W.shape[0] = B * Hq * S;
+    W.shape[0] = (int64_t)(need / 4);
     W.stride[0] = 1;
     for (const chain_tensor *t : ins)
       if (overlap(W, *t)) return fail(CHAIN_ERR_ALIAS, "workspace overlaps a tensor");
@@ -430,7 +433,7 @@ chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const 
   p.q = Q->data, p.k = K->data, p.v = V->data, p.o = O->data, p.dout = dO->data;
   p.lse = (const float *)LSE->data;
   p.dq = (float *)dQ->data, p.dk = (float *)dK->data, p.dv = (float *)dV->data;
-  p.drow = (float *)workspace;
+  p.rowv = (float *)workspace;
   p.q_sb = Q->stride[0], p.q_sh = Q->stride[1], p.q_ss = Q->stride[2];
   p.k_sb = K->stride[0], p.k_sh = K->stride[1], p.k_ss = K->stride[2];
   p.v_sb = V->stride[0], p.v_sh = V->stride[1], p.v_ss = V->stride[2];

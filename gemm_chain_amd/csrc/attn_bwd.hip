@@ -12,21 +12,26 @@
 //
 // Three kernels, no atomics (every output element is written once, so reruns
 // give identical bits):
-//  - rowdot: D_i for every query row into the workspace.
-//  - dq: a workgroup of four waves (one per SIMD) takes 32-row query blocks of
-//    WH heads of one key/value head and walks the visible 64-key tiles, staged
-//    in LDS.  Per tile and wave: S^T = K.Q^T and dP^T = V.dO^T (Q and dO
-//    fragments stay in registers; each lane owns one query, as in the
-//    forward), dS^T = P^T * (dP^T - D) in registers, then dQ^T += K^T.dS^T with
-//    K^T read by ds_read_b64_tr_b16 in the key order the dS^T accumulator holds.
-//  - dkdv: a workgroup of four waves takes 128 keys of one key/value head (32
-//    per wave, their K and V fragments in registers) and walks every visible
-//    32-row query tile of every query head of the group, staged in LDS with its
-//    log-sum-exp and D values.  Per tile and wave: S = Q.K^T and dP = dO.V^T,
-//    P and dS, then dV^T += dO^T.P and dK^T += Q^T.dS with dO^T and Q^T read
-//    transposed.
-// Query tiles (dq) and key blocks (dkdv) are taken in pairs t, T-1-t so causal
-// work per workgroup is even, and workgroups of one key/value head share an XCD.
+//  - rowdot: per query row, D_i and LSE_i * log2(e) into the workspace, in
+//    blocks of 16 rows [16 x LSE*log2e | 16 x D], rows padded to a multiple of
+//    64 with (+inf, 0) so that padding rows get probability 0.
+//  - dq: eight waves (two per SIMD) take 32-row query blocks of WH heads of one
+//    key/value head and walk the visible 64-key tiles.  Per tile and wave:
+//    S^T = K.Q^T and dP^T = V.dO^T (Q and dO fragments stay in registers, each
+//    lane owns one query), dS^T = P^T * (dP^T - D) in registers, then
+//    dQ^T += K^T.dS^T with K^T read by ds_read_b64_tr_b16 in the key order the
+//    dS^T accumulator holds.
+//  - dkdv: four waves (one per SIMD, for the two 32-key accumulators) take 128
+//    keys of one key/value head, 32 per wave with their K and V fragments in
+//    registers, and walk every visible 64-row query tile of every query head of
+//    the group.  Per tile and wave: S = Q.K^T and dP = dO.V^T, P and dS, then
+//    dV^T += dO^T.P and dK^T += Q^T.dS with dO^T and Q^T read transposed.
+// Tiles reach LDS by buffer loads that write LDS directly, into a ring of four
+// stages fetched three tiles ahead, one barrier per tile.  A staged row's
+// 16-byte chunks are XOR-swizzled so that both the 16-byte row-fragment reads
+// and the transposing reads of the same tile hit distinct bank groups.  Query
+// tiles (dq) and key blocks (dkdv) are taken in pairs t, T-1-t so causal work
+// per workgroup is even, and workgroups of one key/value head share an XCD.
 #include "internal.h"
 
 namespace chain {
@@ -37,8 +42,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kAhead = 4;    // LDS fragments in flight ahead of their MFMA
+constexpr int kRowPad = 64;  // workspace rows per head are padded to this multiple
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -46,40 +54,112 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // Transposing LDS read: in each group of 16 lanes, lane i receives element i%4
 // of the 4-element rows addressed by lanes 4e + i/4, e = 0..3.
-__device__ inline i16x4 ds_read_tr(const __bf16 *p) {
+__device__ inline i16x4 ds_read_tr(const char *p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
-// A-operand fragment of T^T for a row-major tile T (pitch `pitch`): columns
-// c0 + lane%32 of T, rows r0 + {4h..4h+3, 8+4h..8+4h+3} for lane half h -- the
-// row order in which a 32x32 accumulator packed by pack_half() holds them.
-__device__ inline bf16x8 tr_frag(const __bf16 *t, int pitch, int r0, int c0, int trow, int tcol) {
-  const __bf16 *a = t + (r0 + trow) * pitch + c0 + tcol;
-  const i16x4 lo = ds_read_tr(a);
-  const i16x4 hi = ds_read_tr(a + 8 * pitch);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Rows 16*hh .. 16*hh + 15 of a 32x32 accumulator (registers 8*hh .. 8*hh + 7),
-// rounded to bf16: the B operand of a product that contracts over those rows.
-__device__ inline bf16x8 pack_half(const f32x16 &c, int hh) {
-  bf16x8 r;
+// Chunk swizzle of a staged tile row r (16-byte chunks, D/8 per row).  Bits 2-3
+// of the D=128 form differ over any 4 aligned rows (the rows one transposing
+// read touches per 32 lanes, over 4 consecutive chunks), and the whole form is
+// a bijection over 16 consecutive rows (the rows 16 lanes of a 16-byte
+// fragment read touch, all at one chunk).  For D=64 two rows share a 256-byte
+// bank window, so the same holds with r/2 in place of r.
+template <int D>
+__device__ inline int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// N MFMAs whose A operands are 16-byte LDS reads at addr(i), each read kAhead
+// MFMAs before its use; op(i, a) issues MFMA i.
+template <int N, typename Addr, typename Op>
+__device__ __forceinline__ void run_b128(Addr addr, Op op) {
+  constexpr int A = N < kAhead ? N : kAhead;
+  bf16x8 f[A];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (__bf16)c[8 * hh + j];
-  return r;
+  for (int i = 0; i < A; ++i) f[i] = *(const bf16x8 *)addr(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 a = f[i % A];
+    if (i + A < N) f[i % A] = *(const bf16x8 *)addr(i + A);
+    op(i, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
-// ---- D_i = sum_d dO_id O_id ------------------------------------------------
+// N MFMAs whose A operands come from two transposing reads each, at lo(i) and
+// hi(i) (k rows r..r+3 / r+8..r+11 of the lane's 16-row group).
+template <int N, typename Lo, typename Hi, typename Op>
+__device__ __forceinline__ void run_tr(Lo lo, Hi hi, Op op) {
+  constexpr int A = N < kAhead ? N : kAhead;
+  i16x4 fl[A], fh[A];
+#pragma unroll
+  for (int i = 0; i < A; ++i) {
+    fl[i] = ds_read_tr(lo(i));
+    fh[i] = ds_read_tr(hi(i));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const i16x8 a = __builtin_shufflevector(fl[i % A], fh[i % A], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (i + A < N) {
+      fl[i % A] = ds_read_tr(lo(i + A));
+      fh[i % A] = ds_read_tr(hi(i + A));
+    }
+    op(i, __builtin_bit_cast(bf16x8, a));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Per-lane LDS byte offsets of the fragments of a staged tile with row pitch
+// 2D bytes: aoff[ks] for the 16-byte row fragment of k-step ks (row l32, chunk
+// 2ks + h2), tlo/thi[db] for the transposing reads of column block db (rows
+// trow and trow + 8 of a 16-row-aligned group).
+template <int D>
+struct FragOffsets {
+  static constexpr int KS = D / 16, DB = D / 32, RB = 2 * D;
+  int aoff[KS], tlo[DB], thi[DB];
+  __device__ __forceinline__ explicit FragOffsets(int lane) {
+    const int h2 = lane >> 5, l32 = lane & 31;
+    const int xa = swz<D>(l32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aoff[ks] = l32 * RB + (((2 * ks + h2) ^ xa) << 4);
+    const int trow = 4 * h2 + ((lane & 15) >> 2);
+    const int ylane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      tlo[db] = trow * RB + (((4 * db + ylane) ^ swz<D>(trow)) << 4) + 8 * (lane & 1);
+      thi[db] = (trow + 8) * RB + (((4 * db + ylane) ^ swz<D>(trow + 8)) << 4) + 8 * (lane & 1);
+    }
+  }
+};
+
+__device__ inline int padded_rows(int S) { return (S + kRowPad - 1) / kRowPad * kRowPad; }
+
+// Float index of row r's LSE*log2e in its head's workspace block; D_i is 16 further.
+__device__ inline int rv_index(int r) { return (r >> 4) * 32 + (r & 15); }
+
+// ---- D_i and LSE_i * log2(e) -------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const AttnBwdParams p) {
   constexpr int CPR = D / 8, RPB = 256 / CPR;
-  const int64_t rows = (int64_t)p.B * p.Hq * p.S;
+  const int Sp = padded_rows(p.S);
+  const int64_t rows = (int64_t)p.B * p.Hq * Sp;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
   const int c = threadIdx.x % CPR;
+  const int s = (int)(row % Sp);
+  const int64_t bh = row / Sp;
+  const bool real = row < rows && s < p.S;
+  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
   float acc = 0.f;
-  if (row < rows) {
-    const int s = (int)(row % p.S), h = (int)((row / p.S) % p.Hq), b = (int)(row / ((int64_t)p.S * p.Hq));
+  if (real) {
     const bf16x8 o = *(const bf16x8 *)((const __bf16 *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)s * p.o_ss + 8 * c);
     const bf16x8 g = *(const bf16x8 *)((const __bf16 *)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)s * p.do_ss + 8 * c);
 #pragma unroll
@@ -87,22 +167,33 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const AttnBwdParams p) {
   }
 #pragma unroll
   for (int w = CPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, CPR);
-  if (row < rows && c == 0) p.drow[row] = acc;
+  if (row < rows && c == 0) {
+    float l2 = INFINITY;   // padding rows and rows without a visible key: probability 0
+    if (real) {
+      const float lse = p.lse[b * p.l_sb + h * p.l_sh + (int64_t)s * p.l_ss];
+      if (lse != -INFINITY) l2 = lse * kLog2e;
+    }
+    float *blk = p.rowv + bh * Sp * 2;
+    blk[rv_index(s)] = l2;
+    blk[rv_index(s) + 16] = real ? acc : 0.f;
+  }
 }
 
 // ---- dQ ----------------------------------------------------------------------
 template <int D, int WH>
 __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
-  constexpr int NW = 4, WQ = NW / WH, ROWS = 32 * WQ;
-  constexpr int KS = D / 16, DB = D / 32, BN = 64;
-  constexpr int LDT = D + 8;                        // staged K and V pitch
-  constexpr int CPR = D / 8;
-  constexpr int LOADS = BN * CPR / (NW * 64);
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BN * LDT];   // [buffer][K, V]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = 8, WQ = NW / WH, ROWS = 32 * WQ, BN = 64;
+  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, CPR = D / 8, RPL = 64 / CPR;
+  constexpr int TB = BN * RB;            // bytes of one staged K or V tile
+  constexpr int SB = 2 * TB;             // a stage: K tile, then V tile
+  constexpr int NST = 4;
+  constexpr int LPW = BN / RPL / NW;     // 1 KB loads per wave and operand
+  constexpr int LT = 2 * LPW;            // per stage
+  static_assert(LPW * RPL * NW == BN, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char lds[NST * SB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int trow = 4 * h2 + ((lane & 15) >> 2);
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   const int group = p.Hq / p.Hkv;
   const int n_hg = p.Hq / WH;
@@ -115,9 +206,25 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
   const int head = hg * WH + wave % WH;
   const int kvh = (hg * WH) / group;
   const int qblk = wave / WH;
-  const __bf16 *kbase = (const __bf16 *)p.k + b * p.k_sb + kvh * p.k_sh;
-  const __bf16 *vbase = (const __bf16 *)p.v + b * p.v_sb + kvh * p.v_sh;
   const float c = p.scale_log2;
+  const int Sp = padded_rows(p.S);
+
+  // Buffer descriptors over this head's K and V rows (the host checks that a
+  // head's rows span less than 2^31 bytes).
+  const uint32_t kss2 = (uint32_t)p.k_ss * 2u, vss2 = (uint32_t)p.v_ss * 2u;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const __bf16 *)p.k + b * p.k_sb + kvh * p.k_sh), 0,
+      (int)((uint32_t)(p.S - 1) * kss2 + 2 * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const __bf16 *)p.v + b * p.v_sb + kvh * p.v_sh), 0,
+      (int)((uint32_t)(p.S - 1) * vss2 + 2 * D), 0x00020000);
+  int lrow[LPW], lch[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    lrow[q] = (wave * LPW + q) * RPL + lane / CPR;
+    lch[q] = (lane % CPR) ^ swz<D>(lrow[q]);
+  }
+  const FragOffsets<D> fo(lane);
 
   for (int pass = 0; pass < 2; ++pass) {
     const int t = pass == 0 ? pr : T - 1 - pr;
@@ -140,84 +247,71 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
         dof[ks] = row_ok ? *(const bf16x8 *)(gr + 16 * ks) : bf16x8{};
       }
     }
-    const float lse = p.lse[b * p.l_sb + head * p.l_sh + (int64_t)rr * p.l_ss];
-    // no visible key (LSE = -inf): every probability is 0
-    const float lse2 = (row_ok && lse != -INFINITY) ? lse * kLog2e : INFINITY;
-    const float drow = p.drow[((int64_t)b * p.Hq + head) * p.S + rr];
+    const float *rv = p.rowv + ((int64_t)b * p.Hq + head) * Sp * 2;
+    const float lse2 = row_ok ? rv[rv_index(rr)] : INFINITY;
+    const float drow = row_ok ? rv[rv_index(rr) + 16] : 0.f;
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
     const int nkt = p.causal ? wg_qmax / BN + 1 : (p.S + BN - 1) / BN;
-    uint4 kr[LOADS], vr[LOADS];
-    auto gload = [&](int kt) {
+    auto issue = [&](int kt, int st) {
+      char *sb = lds + st * SB;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int ci = tid + i * NW * 64;
-        const int key = kt * BN + ci / CPR, c8 = ci % CPR;
-        if (key < p.S) {
-          kr[i] = *(const uint4 *)(kbase + (int64_t)key * p.k_ss + c8 * 8);
-          vr[i] = *(const uint4 *)(vbase + (int64_t)key * p.v_ss + c8 * 8);
-        } else {
-          kr[i] = make_uint4(0, 0, 0, 0);
-          vr[i] = make_uint4(0, 0, 0, 0);
-        }
+      for (int q = 0; q < LPW; ++q) {
+        const uint32_t key = (uint32_t)min(kt * BN + lrow[q], p.S - 1);
+        char *dst = sb + (wave * LPW + q) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)dst, 16, key * kss2 + 16 * lch[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(dst + TB), 16, key * vss2 + 16 * lch[q], 0, 0, 0);
       }
     };
-    auto swrite = [&](int buf) {
+    auto compute = [&](int kt, int st) {
+      const int k0 = kt * BN;
+      if (!wave_rows || (p.causal && k0 > w_qmax)) return;
+      const char *sb = lds + st * SB;
+      const bool full = k0 + BN <= p.S && (!p.causal || k0 + BN - 1 <= row0);
+      const int lim = p.causal ? min(p.S - 1, my_row) : p.S - 1;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int ci = tid + i * NW * 64;
-        *(uint4 *)(&smem[buf][0][(ci / CPR) * LDT + (ci % CPR) * 8]) = kr[i];
-        *(uint4 *)(&smem[buf][1][(ci / CPR) * LDT + (ci % CPR) * 8]) = vr[i];
+      for (int kb = 0; kb < 2; ++kb) {
+        if (p.causal && k0 + 32 * kb > w_qmax) continue;
+        const char *kt_ = sb + kb * 32 * RB;
+        f32x16 s = f32x16{}, dp = f32x16{};
+        run_b128<KS>([&](int i) { return kt_ + fo.aoff[i]; },
+                     [&](int i, bf16x8 a) { s = mfma32(a, qf[i], s); });
+        run_b128<KS>([&](int i) { return kt_ + TB + fo.aoff[i]; },
+                     [&](int i, bf16x8 a) { dp = mfma32(a, dof[i], dp); });
+        // lane (h2, l32) holds key k0 + 32kb + 8(r/4) + 4h2 + r%4 of query my_row
+        bf16x8 dsk[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+          if (!full) x = k0 + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3) <= lim ? x : 0.f;
+          dsk[r >> 3][r & 7] = (__bf16)(x * (dp[r] - drow));
+        }
+        // dQ^T += K^T . dS^T over this block's 32 keys
+        run_tr<2 * DB>([&](int i) { return kt_ + (i & 1) * 16 * RB + fo.tlo[i >> 1]; },
+                       [&](int i) { return kt_ + (i & 1) * 16 * RB + fo.thi[i >> 1]; },
+                       [&](int i, bf16x8 a) { acc[i >> 1] = mfma32(a, dsk[i & 1], acc[i >> 1]); });
       }
     };
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
+    // Ring of NST stages (tile j in stage j % NST), fetched three tiles ahead;
+    // past the last tile the free stage is refilled with the current tile so
+    // every step has the same number of loads in flight.  Stage j+3 is the
+    // stage of tile j-1, whose reads finished before the previous barrier.
+    issue(0, 0);
+    issue(min(1, nkt - 1), 1);
+    issue(min(2, nkt - 1), 2);
+    wait_vmcnt<2 * LT>();
+    __builtin_amdgcn_s_barrier();
     for (int kt = 0; kt < nkt; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nkt) gload(kt + 1);
-      const int k0 = kt * BN;
-      const bool live = wave_rows && (!p.causal || k0 <= w_qmax);
-      if (live) {
-        const __bf16 *ks = smem[buf][0];
-        const __bf16 *vs = smem[buf][1];
-        f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) {
-          const int off = ((i & 1) * 32 + l32) * LDT + (i >> 1) * 16 + 8 * h2;
-          s[i & 1] = mfma32(*(const bf16x8 *)(ks + off), qf[i >> 1], s[i & 1]);
-          dp[i & 1] = mfma32(*(const bf16x8 *)(vs + off), dof[i >> 1], dp[i & 1]);
-        }
-        // lane (h2, l32) holds key k0 + kb*32 + 8*(r/4) + 4*h2 + r%4 of query my_row
-        f32x16 ds[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            const bool vis = key < p.S && (!p.causal || key <= my_row);
-            const float pr_ = vis ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -lse2)) : 0.f;
-            ds[kb][r] = pr_ * (dp[kb][r] - drow);
-          }
-        // dQ^T += K^T . dS^T
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-              acc[db] = mfma32(tr_frag(ks, LDT, kb * 32 + 16 * hh, db * 32, trow, tcol), pack_half(ds[kb], hh), acc[db]);
-      }
-      // buf ^ 1 was last read before the previous step's barrier
-      if (kt + 1 < nkt) {
-        swrite(buf ^ 1);
-        __syncthreads();
-      }
+      issue(kt + 3 < nkt ? kt + 3 : kt, (kt + 3) % NST);
+      compute(kt, kt % NST);
+      wait_vmcnt<2 * LT>();   // this wave's part of tile kt+1 has landed
+      __builtin_amdgcn_s_barrier();
     }
-    __syncthreads();
+    wait_vmcnt<0>();   // no load into LDS may outlive the pass
+    __builtin_amdgcn_s_barrier();
 
     if (row_ok) {
       float *dqr = p.dq + b * p.dq_sb + head * p.dq_sh + (int64_t)my_row * p.dq_ss;
@@ -237,17 +331,19 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
 // ---- dK, dV ------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
-  constexpr int NW = 4, KB = 32 * NW, QT = 32;
-  constexpr int KS = D / 16, DB = D / 32;
-  constexpr int LDT = D + 8;                        // staged Q and dO pitch
-  constexpr int CPR = D / 8;
-  constexpr int LOADS = QT * CPR / (NW * 64);
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][QT * LDT];   // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][QT];          // [buffer][LSE*log2e, D]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = 4, KB = 32 * NW, QT = 64;
+  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, CPR = D / 8, RPL = 64 / CPR;
+  constexpr int TB = QT * RB;            // bytes of one staged Q or dO tile
+  constexpr int SB = 2 * TB + 512;       // a stage: Q, dO, then the tile's row values
+  constexpr int NST = 4;
+  constexpr int LPW = QT / RPL / NW;     // 1 KB loads per wave and operand
+  constexpr int LT = 2 * LPW + 1;        // per stage (one row-value load per wave)
+  static_assert(LPW * RPL * NW == QT, "tile must split evenly over the waves");
+  static_assert(QT == kRowPad, "a query tile's row values are one padded block");
+  __shared__ __attribute__((aligned(1024))) char lds[NST * SB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int trow = 4 * h2 + ((lane & 15) >> 2);
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   const int group = p.Hq / p.Hkv;
   const int NB = (p.S + KB - 1) / KB;
@@ -257,7 +353,18 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
   const int kvh = (item / n_pairs) % p.Hkv;
   const int b = item / (n_pairs * p.Hkv);
   const float c = p.scale_log2;
-  const int nqt = (p.S + QT - 1) / QT;
+  const int Sp = padded_rows(p.S);
+  const int nqt = Sp / QT;
+  const uint32_t qss2 = (uint32_t)p.q_ss * 2u, dss2 = (uint32_t)p.do_ss * 2u;
+  const int qbytes = (int)((uint32_t)(p.S - 1) * qss2 + 2 * D);
+  const int dbytes = (int)((uint32_t)(p.S - 1) * dss2 + 2 * D);
+  int lrow[LPW], lch[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    lrow[q] = (wave * LPW + q) * RPL + lane / CPR;
+    lch[q] = (lane % CPR) ^ swz<D>(lrow[q]);
+  }
+  const FragOffsets<D> fo(lane);
 
   for (int pass = 0; pass < 2; ++pass) {
     const int blk = pass == 0 ? pr : NB - 1 - pr;
@@ -283,103 +390,89 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) dva[db] = f32x16{}, dka[db] = f32x16{};
 
-    // (head of the group, query tile): the tiles that can see a key of the block
+    // steps: (query head of the group, query tile) over the tiles that can see
+    // a key of the block
     const int t0 = p.causal ? kb0 / QT : 0;
     const int per_head = nqt - t0;
     const int steps = group * per_head;
-    uint4 qr[LOADS], gr[LOADS];
-    float rv = 0.f;
-    auto gload = [&](int st) {
-      const int head = kvh * group + st / per_head;
-      const int q0 = (t0 + st % per_head) * QT;
-      const __bf16 *qb = (const __bf16 *)p.q + b * p.q_sb + head * p.q_sh;
-      const __bf16 *gb = (const __bf16 *)p.dout + b * p.do_sb + head * p.do_sh;
+    auto issue = [&](int st_i, int st) {
+      const int head = kvh * group + st_i / per_head;
+      const int t = t0 + st_i % per_head;
+      const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((const __bf16 *)p.q + b * p.q_sb + head * p.q_sh), 0, qbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((const __bf16 *)p.dout + b * p.do_sb + head * p.do_sh), 0, dbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(p.rowv + ((int64_t)b * p.Hq + head) * Sp * 2), 0, Sp * 8, 0x00020000);
+      char *sb = lds + st * SB;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int ci = tid + i * NW * 64;
-        const int row = q0 + ci / CPR, c8 = ci % CPR;
-        if (row < p.S) {
-          qr[i] = *(const uint4 *)(qb + (int64_t)row * p.q_ss + c8 * 8);
-          gr[i] = *(const uint4 *)(gb + (int64_t)row * p.do_ss + c8 * 8);
-        } else {
-          qr[i] = make_uint4(0, 0, 0, 0);
-          gr[i] = make_uint4(0, 0, 0, 0);
-        }
+      for (int q = 0; q < LPW; ++q) {
+        const uint32_t row = (uint32_t)min(t * QT + lrow[q], p.S - 1);
+        char *dst = sb + (wave * LPW + q) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)dst, 16, row * qss2 + 16 * lch[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void *)(dst + TB), 16, row * dss2 + 16 * lch[q], 0, 0, 0);
       }
-      if (tid < 2 * QT) {
-        const int row = q0 + (tid % QT);
-        if (row >= p.S) {
-          rv = tid < QT ? INFINITY : 0.f;   // padding rows: probability 0
-        } else if (tid < QT) {
-          const float lse = p.lse[b * p.l_sb + head * p.l_sh + (int64_t)row * p.l_ss];
-          rv = lse == -INFINITY ? INFINITY : lse * kLog2e;
-        } else {
-          rv = p.drow[((int64_t)b * p.Hq + head) * p.S + row];
-        }
-      }
+      // 512 bytes of row values: 128 per wave, lanes 0..7
+      if (lane < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void *)(sb + 2 * TB + 128 * wave), 16,
+                                                 t * QT * 8 + 128 * wave + 16 * lane, 0, 0, 0);
     };
-    auto swrite = [&](int buf) {
+    auto compute = [&](int st_i, int st) {
+      if (!wave_keys) return;
+      const int q0 = (t0 + st_i % per_head) * QT;
+      const char *sb = lds + st * SB;
+      const float *rv = (const float *)(sb + 2 * TB);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int ci = tid + i * NW * 64;
-        *(uint4 *)(&smem[buf][0][(ci / CPR) * LDT + (ci % CPR) * 8]) = qr[i];
-        *(uint4 *)(&smem[buf][1][(ci / CPR) * LDT + (ci % CPR) * 8]) = gr[i];
-      }
-      if (tid < 2 * QT) rowv[buf][tid / QT][tid % QT] = rv;
-    };
-
-    if (steps > 0) {
-      gload(0);
-      swrite(0);
-    }
-    __syncthreads();
-    for (int st = 0; st < steps; ++st) {
-      const int buf = st & 1;
-      if (st + 1 < steps) gload(st + 1);
-      const int q0 = (t0 + st % per_head) * QT;
-      const bool live = wave_keys && (!p.causal || q0 + QT - 1 >= kw0);
-      if (live) {
-        const __bf16 *qs = smem[buf][0];
-        const __bf16 *gs = smem[buf][1];
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qf0 = q0 + 32 * qb;
+        if (p.causal && qf0 + 31 < kw0) continue;   // every query precedes every key
+        const bool diag = p.causal && qf0 < kw0 + 31;
+        const char *qt_ = sb + qb * 32 * RB;
         f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = l32 * LDT + ks * 16 + 8 * h2;
-          s = mfma32(*(const bf16x8 *)(qs + off), kf[ks], s);
-          dp = mfma32(*(const bf16x8 *)(gs + off), vf[ks], dp);
-        }
-        // lane (h2, l32) holds query q0 + 8*(r/4) + 4*h2 + r%4 of key my_key
-        f32x16 pm, dsm;
+        run_b128<KS>([&](int i) { return qt_ + fo.aoff[i]; },
+                     [&](int i, bf16x8 a) { s = mfma32(a, kf[i], s); });
+        run_b128<KS>([&](int i) { return qt_ + TB + fo.aoff[i]; },
+                     [&](int i, bf16x8 a) { dp = mfma32(a, vf[i], dp); });
+        // lane (h2, l32) holds query qf0 + 8(r/4) + 4h2 + r%4 of key my_key
+        bf16x8 pk[2], dsk[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *(const f32x4 *)(&rowv[buf][0][8 * g + 4 * h2]);
-          const f32x4 d4 = *(const f32x4 *)(&rowv[buf][1][8 * g + 4 * h2]);
+          const int ri = rv_index(32 * qb + 8 * g + 4 * h2);
+          const f32x4 l4 = *(const f32x4 *)(rv + ri);
+          const f32x4 d4 = *(const f32x4 *)(rv + ri + 16);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            const int q = q0 + 8 * g + 4 * h2 + e;
-            const bool vis = key_ok && (!p.causal || my_key <= q);
-            const float pr_ = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[e])) : 0.f;
-            pm[r] = pr_;
-            dsm[r] = pr_ * (dp[r] - d4[e]);
+            float x = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[e]));
+            if (diag) x = my_key <= qf0 + 8 * g + 4 * h2 + e ? x : 0.f;
+            pk[r >> 3][r & 7] = (__bf16)x;
+            dsk[r >> 3][r & 7] = (__bf16)(x * (dp[r] - d4[e]));
           }
         }
-        // dV^T += dO^T . P and dK^T += Q^T . dS (contraction over the tile's queries)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            dva[db] = mfma32(tr_frag(gs, LDT, 16 * hh, db * 32, trow, tcol), pack_half(pm, hh), dva[db]);
-            dka[db] = mfma32(tr_frag(qs, LDT, 16 * hh, db * 32, trow, tcol), pack_half(dsm, hh), dka[db]);
-          }
+        // dV^T += dO^T . P and dK^T += Q^T . dS over this block's 32 queries
+        run_tr<2 * DB>([&](int i) { return qt_ + TB + (i & 1) * 16 * RB + fo.tlo[i >> 1]; },
+                       [&](int i) { return qt_ + TB + (i & 1) * 16 * RB + fo.thi[i >> 1]; },
+                       [&](int i, bf16x8 a) { dva[i >> 1] = mfma32(a, pk[i & 1], dva[i >> 1]); });
+        run_tr<2 * DB>([&](int i) { return qt_ + (i & 1) * 16 * RB + fo.tlo[i >> 1]; },
+                       [&](int i) { return qt_ + (i & 1) * 16 * RB + fo.thi[i >> 1]; },
+                       [&](int i, bf16x8 a) { dka[i >> 1] = mfma32(a, dsk[i & 1], dka[i >> 1]); });
       }
-      // buf ^ 1 was last read before the previous step's barrier
-      if (st + 1 < steps) {
-        swrite(buf ^ 1);
-        __syncthreads();
-      }
+    };
+
+    // Same ring as the dq kernel (steps >= 1: the last query tile sees every key).
+    issue(0, 0);
+    issue(min(1, steps - 1), 1);
+    issue(min(2, steps - 1), 2);
+    wait_vmcnt<2 * LT>();
+    __builtin_amdgcn_s_barrier();
+    for (int st_i = 0; st_i < steps; ++st_i) {
+      issue(st_i + 3 < steps ? st_i + 3 : st_i, (st_i + 3) % NST);
+      compute(st_i, st_i % NST);
+      wait_vmcnt<2 * LT>();
+      __builtin_amdgcn_s_barrier();
     }
-    __syncthreads();
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
 
     if (key_ok) {
       float *dkr = p.dk + b * p.dk_sb + kvh * p.dk_sh + (int64_t)my_key * p.dk_ss;
@@ -403,11 +496,11 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
 
 // One plain kernel per configuration (the bodies are templates).
 #define CHAIN_BWD_KERNELS(D)                                                                            \
-  __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))          \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2)))            \
   void attn_bwd_dq_kernel_d##D##_g1(const AttnBwdParams p) { dq_body<D, 1>(p); }                        \
-  __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))          \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2)))            \
   void attn_bwd_dq_kernel_d##D##_g2(const AttnBwdParams p) { dq_body<D, 2>(p); }                        \
-  __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))          \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2)))            \
   void attn_bwd_dq_kernel_d##D##_g4(const AttnBwdParams p) { dq_body<D, 4>(p); }                        \
   __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))          \
   void attn_bwd_dkdv_kernel_d##D(const AttnBwdParams p) { dkdv_body<D>(p); }
@@ -417,17 +510,18 @@ CHAIN_BWD_KERNELS(128)
 
 template <int D>
 hipError_t launch_d(const AttnBwdParams &p, hipStream_t s) {
-  const int64_t rows = (int64_t)p.B * p.Hq * p.S;
+  const int64_t Sp = (p.S + kRowPad - 1) / kRowPad * kRowPad;
+  const int64_t rows = (int64_t)p.B * p.Hq * Sp;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   const int group = p.Hq / p.Hkv;
   const int wh = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-  const int rows_t = 32 * (4 / wh);
+  const int rows_t = 32 * (8 / wh);
   const int T = (p.S + rows_t - 1) / rows_t;
   const dim3 gq(p.B * (p.Hq / wh) * ((T + 1) / 2));
-  if (wh == 4) hipLaunchKernelGGL((D == 64 ? attn_bwd_dq_kernel_d64_g4 : attn_bwd_dq_kernel_d128_g4), gq, dim3(256), 0, s, p);
-  else if (wh == 2) hipLaunchKernelGGL((D == 64 ? attn_bwd_dq_kernel_d64_g2 : attn_bwd_dq_kernel_d128_g2), gq, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((D == 64 ? attn_bwd_dq_kernel_d64_g1 : attn_bwd_dq_kernel_d128_g1), gq, dim3(256), 0, s, p);
+  if (wh == 4) hipLaunchKernelGGL((D == 64 ? attn_bwd_dq_kernel_d64_g4 : attn_bwd_dq_kernel_d128_g4), gq, dim3(512), 0, s, p);
+  else if (wh == 2) hipLaunchKernelGGL((D == 64 ? attn_bwd_dq_kernel_d64_g2 : attn_bwd_dq_kernel_d128_g2), gq, dim3(512), 0, s, p);
+  else hipLaunchKernelGGL((D == 64 ? attn_bwd_dq_kernel_d64_g1 : attn_bwd_dq_kernel_d128_g1), gq, dim3(512), 0, s, p);
   const int NB = (p.S + 127) / 128;
   const dim3 gk(p.B * p.Hkv * ((NB + 1) / 2));
   hipLaunchKernelGGL((D == 64 ? attn_bwd_dkdv_kernel_d64 : attn_bwd_dkdv_kernel_d128), gk, dim3(256), 0, s, p);

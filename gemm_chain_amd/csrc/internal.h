@@ -171,7 +171,8 @@ struct AttnBwdParams {
   const void *q, *k, *v, *o, *dout;   // bf16
   const float *lse;                   // natural log, [B, Hq, S]
   float *dq, *dk, *dv;                // outputs, f32
-  float *drow;                        // workspace: D_i = sum_d dO_id O_id, [B, Hq, S] dense
+  float *rowv;                        // workspace: per (b, h), rows padded to a multiple of 64,
+                                      // blocks of 16 rows [16 x LSE*log2(e) | 16 x D_i]
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;

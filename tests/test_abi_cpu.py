@@ -264,8 +264,8 @@ def _bwd(lib, t, ws, ws_bytes, **over):
 def test_attn_bwd_validation_codes(lib):
     t, ws = _bwd_set()
     need = lib.chain_attn_bwd_workspace_bytes(1, 4, 256)
-    assert need == 4 * 256 * 4
-    assert lib.chain_attn_bwd_workspace_bytes(1, 3, 5) == 256
+    assert need == 4 * 256 * 8                              # rows padded to 64, 8 bytes each
+    assert lib.chain_attn_bwd_workspace_bytes(1, 3, 5) == 3 * 64 * 8
     assert lib.chain_attn_bwd_workspace_bytes(-1, 3, 5) == 0
     G = 2 ** 30
     # Everything else valid: the missing or short workspace is what fails.
@@ -292,6 +292,11 @@ def test_attn_bwd_validation_codes(lib):
     t2["dK"] = td([1, 2, 128, 64], chain.F32, FAKE + 7 * G)
     t2["dV"] = td([1, 2, 128, 64], chain.F32, FAKE + 8 * G)
     assert _bwd(lib, t2, ws, need) == CODES["CHAIN_ERR_SHAPE"]
+    # one head's query rows must span less than 2^31 bytes (32-bit buffer offsets)
+    Qw = td([1, 4, 256, 64], chain.BF16, FAKE + 2 ** 44, stride=[4 * 256 * 2 ** 23, 256 * 2 ** 23, 2 ** 23, 1])
+    Ow = td([1, 4, 256, 64], chain.BF16, FAKE + 2 ** 45, stride=[4 * 256 * 2 ** 23, 256 * 2 ** 23, 2 ** 23, 1])
+    assert _bwd(lib, t, ws, need, Q=Qw) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    assert _bwd(lib, t, ws, need, dO=Ow) == CODES["CHAIN_ERR_UNSUPPORTED"]
     t3, _ = _bwd_set(D=96)
     assert _bwd(lib, t3, ws, need) == CODES["CHAIN_ERR_UNSUPPORTED"]
     # Empty sequence: valid, nothing launched.
