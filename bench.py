@@ -6,8 +6,8 @@ One step = one causal GQA attention forward over the 65536-token workload
 chunks merged on chip), inputs resident in HBM before timing starts.  Prints
 one JSON line: TFLOP/s (causal FLOPs = 4*B*Hq*S*S*D/2), the roofline of the
 attention kernel, the float64 oracle timed on a bounded sample on the host,
-and secondary figures for the other workloads (4096-token MHA, the ring
-share with its log-sum-exp merge, the MLP chain).
+and secondary figures for the other workloads (4096-token MHA forward and
+backward, the ring share with its log-sum-exp merge, the MLP chain).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
        [--no-cpu-baseline]
@@ -119,9 +119,9 @@ def cpu_baseline(w, inputs, budget_s=12.0):
 
 
 def secondary(torch, chain, steps):
-    """Other workloads: MHA 4096, ring share + merge, MLP chain."""
+    """Other workloads: MHA 4096 forward and backward, ring share + merge, MLP chain."""
     import numpy as np
-    from gemm_chain_amd.workloads import WORKLOADS, gen_attention, gen_mlp
+    from gemm_chain_amd.workloads import WORKLOADS, gen_attention, gen_attention_grad, gen_mlp
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     out = {}
@@ -133,7 +133,21 @@ def secondary(torch, chain, steps):
     ms = time_region(torch, lambda: chain.attn_fwd(q, k, v, causal=True, out=o, lse=l), steps, 2, stream)
     tf = attn_flops(w.B, w.Hq, w.S, w.S, w.D) / ms / 1e9
     out[w.name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-    del q, k, v, o, l
+
+    # Backward of the same attention: dQ, dK, dV from (O, LSE) and dO.  FLOPs
+    # counted as five S x S x D products (S and dP recomputed, dV, dQ, dK) over
+    # the causal half: 2.5 x the forward's count.
+    do = gen_attention_grad(w.B, w.Hq, w.S, w.D, w.dtype, 1.0, w.seed + 1000).to(dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    bws = torch.empty(chain.attn_bwd_workspace_bytes(w.B, w.Hq, w.S), dtype=torch.uint8, device=dev)
+    ms = time_region(torch, lambda: chain.attn_bwd(q, k, v, o, l, do, dq=dq, dk=dk, dv=dv, workspace=bws),
+                     steps, 2, stream)
+    tf = 2.5 * attn_flops(w.B, w.Hq, w.S, w.S, w.D) / ms / 1e9
+    out["attn_bwd_" + w.name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                 "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, o, l, do, dq, dk, dv, bws
 
     w = WORKLOADS["ring_share_bf16_h32_s32768_r0of8"]
     q, k, v = gen_attention(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.amp, w.seed)
