@@ -24,7 +24,8 @@ Modules:
   attention -- softmax(scale.Q.K^T + causal mask).V with per-row log-sum-exp
   attention_bwd -- its gradients dQ, dK, dV for an output gradient dO
   merge     -- combination of partial (O, LSE) results
-  mlp       -- act(X.W1).W2 with erf-GeLU, tanh-GeLU or identity
+  mlp       -- act(X.W1).W2 with erf-GeLU, tanh-GeLU, SiLU or identity, and the
+               gated form (act(X.Wg) * (X.Wu)).Wd
   zigzag    -- zigzag shares and chunks of a sequence; visible-pair counts
   brute     -- element-by-element loops (math.fsum / math.exp) for tiny cases
 
@@ -37,12 +38,12 @@ exact float64); that detail is covered only by the tolerance.
 from .attention import attention, attention_rows, visible_mask
 from .attention_bwd import attention_bwd, attention_bwd_loss
 from .merge import lse_merge
-from .mlp import gelu_erf, gelu_tanh, mlp, ACTIVATIONS
+from .mlp import gelu_erf, gelu_tanh, silu, mlp, mlp_gated, ACTIVATIONS
 from .zigzag import (natural_chunk_positions, zigzag_chunk_positions,
                      zigzag_share_positions, visible_pairs)
 
 __all__ = [
     "attention", "attention_rows", "visible_mask", "attention_bwd", "attention_bwd_loss", "lse_merge", "gelu_erf",
-    "gelu_tanh", "mlp", "ACTIVATIONS", "natural_chunk_positions",
+    "gelu_tanh", "silu", "mlp", "mlp_gated", "ACTIVATIONS", "natural_chunk_positions",
     "zigzag_chunk_positions", "zigzag_share_positions", "visible_pairs",
 ]

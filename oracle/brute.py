@@ -54,6 +54,8 @@ def merge_row(o_rows, lses):
 
 
 def gelu(z, form="erf"):
+    if form == "silu":
+        return z / (1.0 + math.exp(-z)) if z >= 0 else z * math.exp(z) / (1.0 + math.exp(z))
     if form == "erf":
         return 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0)))
     if form == "tanh":
@@ -67,4 +69,14 @@ def mlp(x, w1, w2, form="erf"):
     H = [[gelu(math.fsum(x[i][kk] * w1[kk][n] for kk in range(K)), form) for n in range(N)]
          for i in range(M)]
     return [[math.fsum(H[i][n] * w2[n][c] for n in range(N)) for c in range(K2)]
+            for i in range(M)]
+
+
+def mlp_gated(x, wg, wu, wd, form="silu"):
+    """(act(x.wg) * (x.wu)).wd element by element with math.fsum."""
+    x, wg, wu, wd = _tolist(x), _tolist(wg), _tolist(wu), _tolist(wd)
+    M, K, N, K2 = len(x), len(wg), len(wg[0]), len(wd[0])
+    H = [[gelu(math.fsum(x[i][kk] * wg[kk][n] for kk in range(K)), form) *
+          math.fsum(x[i][kk] * wu[kk][n] for kk in range(K)) for n in range(N)] for i in range(M)]
+    return [[math.fsum(H[i][n] * wd[n][c] for n in range(N)) for c in range(K2)]
             for i in range(M)]

@@ -258,6 +258,53 @@ def check_mlp(mlp, brute):
     assert np.max(np.abs(parts - full)) <= 1e-13
 
 
+def check_silu(silu):
+    ln3 = math.log(3.0)
+    # sigmoid(ln 3) = 3/4
+    assert abs(float(silu(ln3)) - 0.75 * ln3) <= 1e-16 * 4
+    assert float(silu(0.0)) == 0.0
+    xs = np.linspace(-30.0, 30.0, 601)
+    # z*s(z) - (-z)*s(-z) = z (s(z) + s(-z) = 1)
+    assert np.max(np.abs(silu(xs) - silu(-xs) - xs)) <= 1e-13
+    # far tails: z for large z, z*e^z for very negative z
+    assert abs(float(silu(40.0)) - 40.0) <= 40.0 * 1e-15
+    assert abs(float(silu(-40.0)) - (-40.0 * math.exp(-40.0))) <= 1e-30
+    # z/2 + z^2/4 + O(z^4) at the origin
+    assert abs(float(silu(1e-8)) - (0.5e-8 + 0.25e-16)) <= 1e-23
+
+
+def check_mlp_gated(mlp_gated, mlp, brute):
+    rng = np.random.default_rng(13)
+    M, K, N, K2 = 6, 5, 4, 3
+    x = rng.standard_normal((M, K))
+    wg = rng.standard_normal((K, N)) * 0.5
+    wu = rng.standard_normal((K, N)) * 0.5
+    wd = rng.standard_normal((N, K2)) * 0.5
+    for act, form in (("silu", "silu"), ("gelu_erf", "erf"), ("identity", "id")):
+        o = mlp_gated(x, wg, wu, wd, act)
+        ob = np.array(brute.mlp_gated(x, wg, wu, wd, form))
+        assert np.max(np.abs(o - ob)) <= 1e-13
+    # up product identically 1 (a column of ones in X, selected by Wu): the plain chain
+    x1 = x.copy()
+    x1[:, 0] = 1.0
+    w_one = np.zeros((K, N))
+    w_one[0, :] = 1.0
+    for act in ("silu", "gelu_erf"):
+        assert np.max(np.abs(mlp_gated(x1, wg, w_one, wd, act) - mlp(x1, wg, wd, act))) <= 1e-13
+    # the activation acts on the gate product only: with the gate product identically 1,
+    # the result is act(1) times the plain linear chain through Wu
+    for act, a1 in (("silu", 1.0 / (1.0 + math.exp(-1.0))), ("identity", 1.0)):
+        ref = a1 * (x1 @ wu) @ wd
+        assert np.max(np.abs(mlp_gated(x1, w_one, wu, wd, act) - ref)) <= 1e-13
+    # identity activation: gate and up are interchangeable
+    assert np.max(np.abs(mlp_gated(x, wg, wu, wd, "identity") - mlp_gated(x, wu, wg, wd, "identity"))) <= 1e-13
+    assert np.all(mlp_gated(np.zeros((M, K)), wg, wu, wd, "silu") == 0.0)
+    # shards of the inner dimension (gate, up and down together) sum to the whole
+    full = mlp_gated(x, wg, wu, wd, "silu")
+    parts = sum(mlp_gated(x, wg[:, s:s + 2], wu[:, s:s + 2], wd[s:s + 2], "silu") for s in range(0, N, 2))
+    assert np.max(np.abs(parts - full)) <= 1e-13
+
+
 # -------------------------------------------------------------------- zigzag
 
 def check_zigzag(zigzag_share_positions, visible_pairs):

@@ -74,3 +74,11 @@ def test_attention_rows_matches_full():
     rows = [0, 5, 39, 17]
     ro, rl = oracle.attention_rows(q, k, v, 1, 3, rows, causal=True, scale=0.3)
     assert np.array_equal(ro, o[1, 3, rows]) and np.array_equal(rl, l[1, 3, rows])
+
+
+def test_silu_closed_forms_and_identities():
+    P.check_silu(oracle.silu)
+
+
+def test_gated_mlp_brute_force_reductions_and_shards():
+    P.check_mlp_gated(oracle.mlp_gated, oracle.mlp, brute)

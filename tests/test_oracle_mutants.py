@@ -165,3 +165,32 @@ def test_zigzag_mutant_caught(monkeypatch):
     monkeypatch.setattr(OZ, "_pieces", bad_pieces)
     assert _count_failures([lambda: P.check_zigzag(OZ.zigzag_share_positions,
                                                    oracle.visible_pairs)]) == 1
+
+
+def test_silu_mutants_caught():
+    """sigmoid without the factor z, and a sign slip inside the exponential."""
+    def no_factor(z):
+        return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+
+    def sign_slip(z):
+        z = np.asarray(z, dtype=np.float64)
+        return z / (1.0 + np.exp(z))
+
+    for bad in (no_factor, sign_slip):
+        assert _count_failures([lambda: P.check_silu(bad)]) == 1
+
+
+def test_gated_mlp_mutants_caught():
+    """Activation on the up product instead of the gate, a missing activation,
+    and gate/up products added instead of multiplied."""
+    def act_on_up(x, wg, wu, wd, act="silu"):
+        return (OMLP.ACTIVATIONS[act](x @ wu) * (x @ wg)) @ wd
+
+    def no_act(x, wg, wu, wd, act="silu"):
+        return ((x @ wg) * (x @ wu)) @ wd
+
+    def added(x, wg, wu, wd, act="silu"):
+        return (OMLP.ACTIVATIONS[act](x @ wg) + (x @ wu)) @ wd
+
+    for bad in (act_on_up, no_act, added):
+        assert _count_failures([lambda: P.check_mlp_gated(bad, oracle.mlp, brute)]) == 1
