@@ -7,7 +7,8 @@ chunks merged on chip), inputs resident in HBM before timing starts.  Prints
 one JSON line: TFLOP/s (causal FLOPs = 4*B*Hq*S*S*D/2), the roofline of the
 attention kernel, the float64 oracle timed on a bounded sample on the host,
 and secondary figures for the other workloads (4096-token MHA forward and
-backward, the ring share with its log-sum-exp merge, the MLP chain).
+backward, the ring share with its log-sum-exp merge, the MLP chain plain and
+gated).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
        [--no-cpu-baseline]
@@ -119,9 +120,10 @@ def cpu_baseline(w, inputs, budget_s=12.0):
 
 
 def secondary(torch, chain, steps):
-    """Other workloads: MHA 4096 forward and backward, ring share + merge, MLP chain."""
+    """Other workloads: MHA 4096 forward and backward, ring share + merge, MLP chain
+    (plain and gated)."""
     import numpy as np
-    from gemm_chain_amd.workloads import WORKLOADS, gen_attention, gen_attention_grad, gen_mlp
+    from gemm_chain_amd.workloads import WORKLOADS, gen_attention, gen_attention_grad, gen_mlp, gen_mlp_gated
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     out = {}
@@ -201,6 +203,21 @@ def secondary(torch, chain, steps):
         res.update({"ms" + tag: round(ms, 4), "tflops" + tag: round(flops / ms / 1e9, 1),
                     "frac_peak" + tag: round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)})
     out[w.name] = res
+    del x, w1, w2, w1c, w2c, o, ws
+
+    # Gated form (gate/up/down shards): H = act(X.Wg) * (X.Wu) in one kernel, then H.Wd;
+    # weights column-major (linear-layer layout).  Three M x K x N products.
+    w = WORKLOADS["mlp_gated_bf16_m16384_k4096_n1376"]
+    x, wg, wu, wd = (t.to(dev) for t in gen_mlp_gated(w.M, w.K, w.N, dtype=w.dtype, amp_x=w.amp_x,
+                                                      amp_w=w.amp_w, seed=w.seed))
+    wg, wu, wd = (t.t().contiguous().t() for t in (wg, wu, wd))
+    o = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(chain.mlp_workspace_bytes(w.M, w.N), dtype=torch.uint8, device=dev)
+    flops = 6.0 * w.M * w.K * w.N
+    ms = time_region(torch, lambda: chain.mlp_gated_fwd(x, wg, wu, wd, act=w.act, out=o, workspace=ws),
+                     steps, 2, stream)
+    out[w.name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                   "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
     return out
 
 

@@ -21,7 +21,7 @@ MAX_RUNS = 4
 
 F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
-ACTS = {"gelu_erf": 0, "gelu_tanh": 1, "identity": 2}
+ACTS = {"gelu_erf": 0, "gelu_tanh": 1, "identity": 2, "silu": 3}
 
 STATUS = ["CHAIN_OK", "CHAIN_ERR_NULL", "CHAIN_ERR_DTYPE", "CHAIN_ERR_SHAPE", "CHAIN_ERR_LAYOUT",
           "CHAIN_ERR_ALIGN", "CHAIN_ERR_ALIAS", "CHAIN_ERR_UNSUPPORTED", "CHAIN_ERR_WORKSPACE",
@@ -70,6 +70,7 @@ def load():
         "chain_lse_merge": (ctypes.c_int, [T, T, T, T, vp]),
         "chain_mlp_fwd": (ctypes.c_int, [T, T, T, T, ctypes.c_int, vp, sz, vp]),
         "chain_mlp_workspace_bytes": (sz, [i64, i64, i32]),
+        "chain_mlp_gated_fwd": (ctypes.c_int, [T, T, T, T, T, ctypes.c_int, vp, sz, vp]),
         "chain_attn_bwd": (ctypes.c_int, [T, T, T, T, T, T, T, T, T, ctypes.c_int, f32, vp, sz, vp]),
         "chain_attn_bwd_workspace_bytes": (sz, [i64, i64, i64]),
         "chain_zigzag_segs": (ctypes.c_int, [i64, i32, i32, S]),
@@ -201,6 +202,19 @@ def mlp_fwd(x, w1, w2, act="gelu_erf", out=None, out_dtype=None, workspace=None)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _check(lib.chain_mlp_fwd(desc(x), desc(w1), desc(w2), desc(o), ACTS[act],
                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(x)))
+    return o
+
+
+def mlp_gated_fwd(x, wg, wu, wd, act="silu", out=None, out_dtype=None, workspace=None):
+    """O = (act(X.Wg) * (X.Wu)).Wd; Wg and Wu column-major [K, N] views."""
+    lib = load()
+    M, N, K2 = x.shape[0], wg.shape[1], wd.shape[1]
+    o = torch.empty((M, K2), dtype=out_dtype or x.dtype, device=x.device) if out is None else out
+    need = mlp_workspace_bytes(M, N, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check(lib.chain_mlp_gated_fwd(desc(x), desc(wg), desc(wu), desc(wd), desc(o), ACTS[act],
+                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(x)))
     return o
 
 

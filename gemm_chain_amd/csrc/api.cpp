@@ -315,7 +315,7 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
   TRY(check_tensor(O, "O", 2, O && O->dtype == CHAIN_F32 ? 4 : 2));
   if (W1->dtype != X->dtype || W2->dtype != X->dtype)
     return fail(CHAIN_ERR_DTYPE, "X, W1 and W2 must share one dtype");
-  if (act != CHAIN_ACT_GELU_ERF && act != CHAIN_ACT_GELU_TANH && act != CHAIN_ACT_IDENTITY)
+  if (act != CHAIN_ACT_GELU_ERF && act != CHAIN_ACT_GELU_TANH && act != CHAIN_ACT_IDENTITY && act != CHAIN_ACT_SILU)
     return fail(CHAIN_ERR_UNSUPPORTED, "unknown activation %d", act);
   const int64_t M = X->shape[0], K = X->shape[1], N = W1->shape[1], K2 = W2->shape[1];
   if (W1->shape[0] != K || W2->shape[0] != N || O->shape[0] != M || O->shape[1] != K2)
@@ -401,7 +401,7 @@ chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const 
   }
   if (B * Hq * S > INT32_MAX) return fail(CHAIN_ERR_UNSUPPORTED, "B * Hq * S beyond 2^31");
   // The kernels address one head's query and dO rows with 32-bit byte offsets.
-  if (S > 0 && ((S - 1) * Q->stride[2] + D) * 2 > INT32_MAX || S > 0 && ((S - 1) * dO->stride[2] + D) * 2 > INT32_MAX)
+  if (S > 0 && (((S - 1) * Q->stride[2] + D) * 2 > INT32_MAX || ((S - 1) * dO->stride[2] + D) * 2 > INT32_MAX))
     return fail(CHAIN_ERR_UNSUPPORTED, "the query or dO rows of one head span 2 GiB or more");
   const chain_tensor *ins[] = {Q, K, V, O, LSE, dO};
   const chain_tensor *outs[] = {dQ, dK, dV};
@@ -448,6 +448,76 @@ chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const 
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = chain::launch_attn_bwd(p, (int)D, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CHAIN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg, const chain_tensor *Wu,
+                                 const chain_tensor *Wd, const chain_tensor *O, int act, void *workspace,
+                                 size_t ws_bytes, void *stream) {
+  TRY(check_tensor(X, "X", 2));
+  TRY(check_tensor(Wg, "Wg", 2, 16, true));
+  TRY(check_tensor(Wu, "Wu", 2, 16, true));
+  TRY(check_tensor(Wd, "Wd", 2, 16, true));
+  TRY(check_tensor(O, "O", 2, O && O->dtype == CHAIN_F32 ? 4 : 2));
+  if (Wg->dtype != X->dtype || Wu->dtype != X->dtype || Wd->dtype != X->dtype)
+    return fail(CHAIN_ERR_DTYPE, "X, Wg, Wu and Wd must share one dtype");
+  if (act != CHAIN_ACT_GELU_ERF && act != CHAIN_ACT_GELU_TANH && act != CHAIN_ACT_IDENTITY && act != CHAIN_ACT_SILU)
+    return fail(CHAIN_ERR_UNSUPPORTED, "unknown activation %d", act);
+  const int64_t M = X->shape[0], K = X->shape[1], N = Wg->shape[1], K2 = Wd->shape[1];
+  if (Wg->shape[0] != K || Wu->shape[0] != K || Wu->shape[1] != N || Wd->shape[0] != N ||
+      O->shape[0] != M || O->shape[1] != K2)
+    return fail(CHAIN_ERR_SHAPE, "expected X[M,K] Wg[K,N] Wu[K,N] Wd[N,K2] O[M,K2]");
+  if (X->dtype != CHAIN_BF16) return fail(CHAIN_ERR_UNSUPPORTED, "the gated form takes bf16 inputs");
+  if (K % 8 || N % 8 || K2 % 8) return fail(CHAIN_ERR_UNSUPPORTED, "K, N and K2 must be multiples of 8");
+  if (M > INT32_MAX || K > INT32_MAX || N > INT32_MAX || K2 > INT32_MAX)
+    return fail(CHAIN_ERR_UNSUPPORTED, "sizes beyond 2^31");
+  // Gate and up weights: k contiguous, one column stride for both.
+  auto kmajor = [](const chain_tensor &w) { return w.shape[0] <= 1 || w.stride[0] == 1; };
+  const int64_t gsn = Wg->shape[1] <= 1 ? K : Wg->stride[1], usn = Wu->shape[1] <= 1 ? K : Wu->stride[1];
+  if (K > 0 && N > 0 && (!kmajor(*Wg) || !kmajor(*Wu) || gsn != usn))
+    return fail(CHAIN_ERR_UNSUPPORTED, "gate and up weights must be column-major with equal strides");
+  if (overlap(*O, *X) || overlap(*O, *Wg) || overlap(*O, *Wu) || overlap(*O, *Wd))
+    return fail(CHAIN_ERR_ALIAS, "O overlaps an input");
+  const size_t need = chain_mlp_workspace_bytes(M, N, CHAIN_BF16);
+  if (M == 0 || K2 == 0) return ok();
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(CHAIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if ((uintptr_t)workspace % 256) return fail(CHAIN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  {
+    chain_tensor H{};
+    H.data = workspace;
+    H.dtype = CHAIN_BF16;
+    H.ndim = 2;
+    H.shape[0] = M, H.shape[1] = N;
+    H.stride[0] = N, H.stride[1] = 1;
+    if (overlap(H, *X) || overlap(H, *Wg) || overlap(H, *Wu) || overlap(H, *Wd) || overlap(H, *O))
+      return fail(CHAIN_ERR_ALIAS, "workspace overlaps a tensor");
+  }
+  const size_t oes = elem_size(O->dtype);
+  chain::GemmParams g1{}, g2{};
+  g1.a = X->data, g1.b = Wg->data, g1.b2 = Wu->data, g1.gated = 1, g1.c = workspace;
+  g1.lda = X->stride[0], g1.ldc = N;
+  g1.b_sk = 1, g1.b_sn = gsn;
+  g1.M = (int32_t)M, g1.N = (int32_t)N, g1.K = (int32_t)K;
+  g1.act = act;
+  g1.c_f32 = 0;
+  g1.c_vec = N % 4 == 0;   // workspace is 256-byte aligned
+  g2.a = workspace, g2.b = Wd->data, g2.c = O->data;
+  g2.lda = N, g2.ldc = O->stride[0];
+  const bool dk = !(Wd->shape[1] <= 1 || Wd->stride[1] == 1);
+  g2.b_sk = dk ? 1 : (Wd->shape[0] <= 1 ? Wd->shape[1] : Wd->stride[0]);
+  g2.b_sn = dk ? Wd->stride[1] : 1;
+  g2.M = (int32_t)M, g2.N = (int32_t)K2, g2.K = (int32_t)N;
+  g2.act = CHAIN_ACT_IDENTITY;
+  g2.c_f32 = O->dtype == CHAIN_F32;
+  g2.c_vec = (uintptr_t)O->data % (4 * oes) == 0 && (M <= 1 || (O->stride[0] * oes) % (4 * oes) == 0);
+  const int64_t kMaxStride = int64_t(1) << 25;   // per-thread offsets within a tile stay 32-bit
+  for (const int64_t st : {g1.lda, g1.b_sn, g2.b_sk, g2.b_sn, g2.ldc})
+    if (st > kMaxStride) return fail(CHAIN_ERR_UNSUPPORTED, "row strides beyond 2^25 elements");
+  hipError_t e = hipSuccess;
+  if (N > 0) e = chain::launch_gemm(g1, CHAIN_BF16, (hipStream_t)stream);
+  if (e == hipSuccess) e = chain::launch_gemm(g2, CHAIN_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return fail(CHAIN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -21,7 +21,10 @@
 //  - n-contiguous B (gemm_bf16_kernel<NBW>): k-tiles of 64 staged through
 //    registers into two LDS buffers; A as [256][64 + 8], B as [64][BN' + 32]
 //    read with ds_read_b64_tr_b16.
-// Both give the same MFMA operands in the same k order.  The f32 path for f32
+// Both give the same MFMA operands in the same k order.  The gated MLP's first
+// product (TSP article: gate and up projection shards) runs the k-contiguous
+// kernel with two B matrices whose tiles share the A tile, and multiplies
+// act(gate) by up in the epilogue.  The f32 path for f32
 // inputs keeps a 128 x 128 x 32 tile per 256 threads with
 // v_mfma_f32_32x32x2_f32.
 #include "internal.h"
@@ -67,6 +70,7 @@ __device__ inline float activate(float z, int act) {
     const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
     return 0.5f * z * (1.f + tanhf(u));
   }
+  if (act == CHAIN_ACT_SILU) return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
   return z;
 }
 
@@ -76,8 +80,9 @@ constexpr int LDA = BK + 8;        // pitch of k-contiguous stages
 __device__ inline u32x4 ld16(const __bf16 *p) { return *(const u32x4 *)p; }
 
 // n-contiguous B (row-major [K, N] weights).  NBW = 32-column blocks per wave
-// (BN = 64 * NBW).
-template <int NBW>
+// (BN = 64 * NBW).  ACT: the epilogue's activation, one instantiation each (a
+// run-time choice among several epilogues costs registers in the main loop).
+template <int NBW, int ACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const GemmParams p) {
   constexpr int BN = 64 * NBW, WTN = 32 * NBW;
@@ -226,8 +231,7 @@ void gemm_bf16_kernel(const GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  auto store_all = [&](auto act_c) {
-    constexpr int ACT = decltype(act_c)::value;
+  auto store_all = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int gm = m0 + wm * 128 + i * 32 + l32;
@@ -255,9 +259,7 @@ void gemm_bf16_kernel(const GemmParams p) {
         }
     }
   };
-  if (p.act == CHAIN_ACT_GELU_ERF) store_all(std::integral_constant<int, CHAIN_ACT_GELU_ERF>{});
-  else if (p.act == CHAIN_ACT_GELU_TANH) store_all(std::integral_constant<int, CHAIN_ACT_GELU_TANH>{});
-  else store_all(std::integral_constant<int, CHAIN_ACT_IDENTITY>{});
+  store_all();
 }
 
 // ---- k-contiguous A and B: direct-to-LDS stage ring ------------------------
@@ -283,9 +285,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-template <int NBW>
+// GATED: the BN staged B rows of a tile are BN/2 output columns of B (gate) and
+// the same BN/2 columns of B2 (up), arranged so that each wave's 32-row blocks
+// alternate gate, up for the same 32 columns: the epilogue then finds the two
+// products of an output element in the same lane and register.
+template <int NBW, bool GATED, int ACT>
 __device__ __forceinline__ void gemm_bf16_dtl(const GemmParams &p) {
   constexpr int BN = 64 * NBW, WTN = 32 * NBW;
+  constexpr int OBN = GATED ? BN / 2 : BN;   // output columns per tile
+  static_assert(!GATED || NBW % 2 == 0, "gated tiles pair 32-row blocks");
   constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
   constexpr int LA = 4, LB = NBW, L = LA + LB;   // 1 KB loads per wave per stage
   __shared__ __attribute__((aligned(1024))) char lds[DST * STAGE];
@@ -296,24 +304,32 @@ __device__ __forceinline__ void gemm_bf16_dtl(const GemmParams &p) {
 
   // Tile order: groups of 4 row blocks x all column blocks, row block fastest,
   // so the 32 tiles an XCD runs at once cover 4 x 8 blocks.
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + OBN - 1) / OBN;
   const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   constexpr int GM = 4;
   const int g = t / (GM * tiles_n), fm = g * GM;
   const int gmn = min(GM, tiles_m - fm), loc = t - g * GM * tiles_n;
-  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * BN;
+  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * OBN;
 
   // Lane i of a load fetches row i >> 2 of its 16-row block, logical chunk lc.
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);
   const __bf16 *A = (const __bf16 *)p.a;
-  const __bf16 *B = (const __bf16 *)p.b;
-  int64_t a_off[LA], b_off[LB];
+  int64_t a_off[LA];
+  const __bf16 *bp[LB];
 #pragma unroll
   for (int q = 0; q < LA; ++q)
     a_off[q] = (int64_t)min(m0 + 16 * (wave * LA + q) + (lane >> 2), p.M - 1) * p.lda + 8 * lc;
 #pragma unroll
-  for (int q = 0; q < LB; ++q)
-    b_off[q] = (int64_t)min(n0 + 16 * (wave * LB + q) + (lane >> 2), p.N - 1) * p.b_sn + 8 * lc;
+  for (int q = 0; q < LB; ++q) {
+    const int rb = 16 * (wave * LB + q) + (lane >> 2);   // staged B row
+    if (GATED) {
+      const int j = (rb % WTN) / 32;   // the wave's 32-row block: even gate, odd up
+      const int col = n0 + (rb / WTN) * (WTN / 2) + (j >> 1) * 32 + rb % 32;
+      bp[q] = (const __bf16 *)(j & 1 ? p.b2 : p.b) + (int64_t)min(col, p.N - 1) * p.b_sn + 8 * lc;
+    } else {
+      bp[q] = (const __bf16 *)p.b + (int64_t)min(n0 + rb, p.N - 1) * p.b_sn + 8 * lc;
+    }
+  }
   const int nk = (p.K + DBK - 1) / DBK;
 
   // Stage kt >= nk (issued so that every loop iteration has the same shape)
@@ -328,7 +344,7 @@ __device__ __forceinline__ void gemm_bf16_dtl(const GemmParams &p) {
       __builtin_amdgcn_global_load_lds(A + a_off[q] + kk, sb + (wave * LA + q) * 1024, 16, 0, 0);
 #pragma unroll
     for (int q = 0; q < LB; ++q)
-      __builtin_amdgcn_global_load_lds(B + b_off[q] + kk, sb + A_BYTES + (wave * LB + q) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bp[q] + kk, sb + A_BYTES + (wave * LB + q) * 1024, 16, 0, 0);
   };
   // After stage kt (the K tail) has landed: zero the chunks past K.
   auto zero_tail = [&](int kt) {
@@ -423,47 +439,69 @@ __device__ __forceinline__ void gemm_bf16_dtl(const GemmParams &p) {
     wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
   }
 
-  auto store_all = [&](auto act_c) {
-    constexpr int ACT = decltype(act_c)::value;
+  auto store4 = [&](int gm, int gn, const f32x4 &v) {
+    const int64_t off = (int64_t)gm * p.ldc + gn;
+    if (p.c_f32) {
+      float *c = (float *)p.c + off;
+      if (p.c_vec) *(f32x4 *)c = v;
+      else c[0] = v[0], c[1] = v[1], c[2] = v[2], c[3] = v[3];
+    } else {
+      __bf16 *c = (__bf16 *)p.c + off;
+      const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      if (p.c_vec) *(bf16x4 *)c = w;
+      else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
+    }
+  };
+  auto store_all = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int gm = m0 + wm * 128 + i * 32 + l32;
       if (gm >= p.M) continue;
+      if constexpr (GATED) {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j)
+        for (int u = 0; u < NBW / 2; ++u)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
-          if (gn >= p.N) continue;
-          f32x4 v;
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int gn = n0 + wn * (WTN / 2) + u * 32 + 8 * r4 + 4 * h2;
+            if (gn >= p.N) continue;
+            f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
-          const int64_t off = (int64_t)gm * p.ldc + gn;
-          if (p.c_f32) {
-            float *c = (float *)p.c + off;
-            if (p.c_vec) *(f32x4 *)c = v;
-            else c[0] = v[0], c[1] = v[1], c[2] = v[2], c[3] = v[3];
-          } else {
-            __bf16 *c = (__bf16 *)p.c + off;
-            const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-            if (p.c_vec) *(bf16x4 *)c = w;
-            else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
+            for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][2 * u][4 * r4 + e], ACT) * acc[i][2 * u + 1][4 * r4 + e];
+            store4(gm, gn, v);
           }
-        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
+            if (gn >= p.N) continue;
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
+            store4(gm, gn, v);
+          }
+      }
     }
   };
-  if (p.act == CHAIN_ACT_GELU_ERF) store_all(std::integral_constant<int, CHAIN_ACT_GELU_ERF>{});
-  else if (p.act == CHAIN_ACT_GELU_TANH) store_all(std::integral_constant<int, CHAIN_ACT_GELU_TANH>{});
-  else store_all(std::integral_constant<int, CHAIN_ACT_IDENTITY>{});
+  store_all();
 }
 
 // One plain kernel per tile width (the body is a template).
-#define CHAIN_DTL_KERNEL(NBW)                                                              \
+#define CHAIN_DTL_KERNEL(NAME, NBW, GATED, ACT)                                            \
   __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) \
-  void gemm_bf16_dtl_kernel_##NBW(const GemmParams p) { gemm_bf16_dtl<NBW>(p); }
-CHAIN_DTL_KERNEL(2)
-CHAIN_DTL_KERNEL(3)
-CHAIN_DTL_KERNEL(4)
+  void NAME(const GemmParams p) { gemm_bf16_dtl<NBW, GATED, ACT>(p); }
+#define CHAIN_DTL_KERNELS(SUFFIX, ACT)                                             \
+  CHAIN_DTL_KERNEL(gemm_bf16_dtl_kernel_2_##SUFFIX, 2, false, ACT)                 \
+  CHAIN_DTL_KERNEL(gemm_bf16_dtl_kernel_3_##SUFFIX, 3, false, ACT)                 \
+  CHAIN_DTL_KERNEL(gemm_bf16_dtl_kernel_4_##SUFFIX, 4, false, ACT)                 \
+  CHAIN_DTL_KERNEL(gemm_bf16_dtl_gated_kernel_2_##SUFFIX, 2, true, ACT)            \
+  CHAIN_DTL_KERNEL(gemm_bf16_dtl_gated_kernel_4_##SUFFIX, 4, true, ACT)
+CHAIN_DTL_KERNELS(erf, CHAIN_ACT_GELU_ERF)
+CHAIN_DTL_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
+CHAIN_DTL_KERNELS(id, CHAIN_ACT_IDENTITY)
+CHAIN_DTL_KERNELS(silu, CHAIN_ACT_SILU)
+#undef CHAIN_DTL_KERNELS
 #undef CHAIN_DTL_KERNEL
 
 // f32 inputs: 128 x 128 x 32 tiles on v_mfma_f32_32x32x2_f32 (A: lane holds
@@ -533,7 +571,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
 template <int NBW>
 void launch_bf16(const GemmParams &p, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * NBW - 1) / (64 * NBW));
-  hipLaunchKernelGGL((gemm_bf16_kernel<NBW>), dim3(tiles), dim3(256), 0, stream, p);
+  switch (p.act) {
+    case CHAIN_ACT_GELU_ERF: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_GELU_ERF>), dim3(tiles), dim3(256), 0, stream, p); break;
+    case CHAIN_ACT_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_GELU_TANH>), dim3(tiles), dim3(256), 0, stream, p); break;
+    case CHAIN_ACT_SILU: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_SILU>), dim3(tiles), dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_IDENTITY>), dim3(tiles), dim3(256), 0, stream, p);
+  }
 }
 
 void launch_bf16_width(const GemmParams &p, int nbw, hipStream_t stream) {
@@ -542,11 +585,32 @@ void launch_bf16_width(const GemmParams &p, int nbw, hipStream_t stream) {
   else launch_bf16<2>(p, stream);
 }
 
+// Gated: 32 * nbw output columns per tile; nbw 4 unless 2 fills the chip's
+// rounds with less work per CU.
+void launch_dtl_gated(const GemmParams &p, int cus, hipStream_t stream) {
+  const int tm = (p.M + BM - 1) / BM;
+  auto cost = [&](int nbw) {
+    const int64_t tiles = (int64_t)tm * ((p.N + 32 * nbw - 1) / (32 * nbw));
+    return ((tiles + cus - 1) / cus) * nbw;
+  };
+  const int nbw = cost(2) < cost(4) ? 2 : 4;
+  const int tiles = tm * ((p.N + 32 * nbw - 1) / (32 * nbw));
+  typedef void (*Kern)(const GemmParams);
+  static const Kern k2[4] = {gemm_bf16_dtl_gated_kernel_2_erf, gemm_bf16_dtl_gated_kernel_2_tanh,
+                             gemm_bf16_dtl_gated_kernel_2_id, gemm_bf16_dtl_gated_kernel_2_silu};
+  static const Kern k4[4] = {gemm_bf16_dtl_gated_kernel_4_erf, gemm_bf16_dtl_gated_kernel_4_tanh,
+                             gemm_bf16_dtl_gated_kernel_4_id, gemm_bf16_dtl_gated_kernel_4_silu};
+  hipLaunchKernelGGL((nbw == 4 ? k4 : k2)[p.act], dim3(tiles), dim3(256), 0, stream, p);
+}
+
 void launch_dtl(const GemmParams &p, int nbw, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * nbw - 1) / (64 * nbw));
-  if (nbw == 4) hipLaunchKernelGGL(gemm_bf16_dtl_kernel_4, dim3(tiles), dim3(256), 0, stream, p);
-  else if (nbw == 3) hipLaunchKernelGGL(gemm_bf16_dtl_kernel_3, dim3(tiles), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(gemm_bf16_dtl_kernel_2, dim3(tiles), dim3(256), 0, stream, p);
+  typedef void (*Kern)(const GemmParams);
+  static const Kern ks[3][4] = {
+      {gemm_bf16_dtl_kernel_2_erf, gemm_bf16_dtl_kernel_2_tanh, gemm_bf16_dtl_kernel_2_id, gemm_bf16_dtl_kernel_2_silu},
+      {gemm_bf16_dtl_kernel_3_erf, gemm_bf16_dtl_kernel_3_tanh, gemm_bf16_dtl_kernel_3_id, gemm_bf16_dtl_kernel_3_silu},
+      {gemm_bf16_dtl_kernel_4_erf, gemm_bf16_dtl_kernel_4_tanh, gemm_bf16_dtl_kernel_4_id, gemm_bf16_dtl_kernel_4_silu}};
+  hipLaunchKernelGGL(ks[nbw - 2][p.act], dim3(tiles), dim3(256), 0, stream, p);
 }
 
 int compute_units() {
@@ -578,7 +642,10 @@ int gemm_bf16_block_cols(int M, int N, int cus) {
 
 hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  if (dtype == CHAIN_BF16) {
+  if (p.gated) {
+    if (dtype != CHAIN_BF16 || p.b_sk != 1) return hipErrorInvalidValue;
+    launch_dtl_gated(p, compute_units(), stream);
+  } else if (dtype == CHAIN_BF16) {
     const int nbw = gemm_bf16_block_cols(p.M, p.N, compute_units());
     if (p.b_sk == 1) {
       launch_dtl(p, nbw, stream);

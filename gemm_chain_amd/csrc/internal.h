@@ -165,6 +165,8 @@ struct GemmParams {
   int32_t act;        // chain_act
   int32_t c_f32;      // 1: C is f32, 0: C is bf16
   int32_t c_vec;      // 1: C rows allow 4-element vector stores (aligned base and ldc)
+  const void *b2;     // gated: the up weights, strides of b (k contiguous); C = act(A.B) * (A.B2)
+  int32_t gated;      // 1: the gated product above (bf16, b_sk == 1 only)
 };
 
 struct AttnBwdParams {

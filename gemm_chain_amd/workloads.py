@@ -52,6 +52,7 @@ class MlpWorkload:
     amp_w: float
     seed: int
     act: str = "gelu_erf"
+    gated: bool = False   # (act(X.Wg) * (X.Wu)).Wd with Wg, Wu [K, N] and Wd [N, K]
 
 
 WORKLOADS = {
@@ -68,6 +69,10 @@ WORKLOADS = {
     # one 8-way shard of an 11008-wide FFN: GeLU(X.W1).W2
     "mlp_bf16_m16384_k4096_n1376": MlpWorkload(
         "mlp_bf16_m16384_k4096_n1376", "bf16", 16384, 4096, 1376, 1.0, 0.02, 4),
+    # one 8-way shard of an 11008-wide gated FFN: (SiLU(X.Wg) * (X.Wu)).Wd
+    "mlp_gated_bf16_m16384_k4096_n1376": MlpWorkload(
+        "mlp_gated_bf16_m16384_k4096_n1376", "bf16", 16384, 4096, 1376, 1.0, 0.02, 6, act="silu",
+        gated=True),
     # long causal GQA attention, 32 query heads over 8 KV heads, 16 zigzag chunks
     "attn_gqa_bf16_h32kv8_s65536_d128": AttnWorkload(
         "attn_gqa_bf16_h32kv8_s65536_d128", "bf16", 1, 32, 8, 65536, 128, 1.0, 5,
@@ -102,10 +107,25 @@ def gen_mlp(M, K, N, K2=None, dtype="bf16", amp_x=1.0, amp_w=0.02, seed=0):
     return x, w1, w2
 
 
+def gen_mlp_gated(M, K, N, K2=None, dtype="bf16", amp_x=1.0, amp_w=0.02, seed=0):
+    """X [M,K], Wg and Wu [K,N], Wd [N,K2] on the CPU, drawn in the order X, Wg, Wu, Wd."""
+    K2 = K if K2 is None else K2
+    g = torch.Generator().manual_seed(seed)
+    dt = _DTYPES[dtype]
+    x = (torch.randn(M, K, generator=g, dtype=torch.float32) * amp_x).to(dt)
+    wg = (torch.randn(K, N, generator=g, dtype=torch.float32) * amp_w).to(dt)
+    wu = (torch.randn(K, N, generator=g, dtype=torch.float32) * amp_w).to(dt)
+    wd = (torch.randn(N, K2, generator=g, dtype=torch.float32) * amp_w).to(dt)
+    return x, wg, wu, wd
+
+
 def workload_inputs(w, S=None):
     """Inputs of a named workload, optionally with a reduced sequence length S."""
     if isinstance(w, str):
         w = WORKLOADS[w]
+    if isinstance(w, MlpWorkload) and w.gated:
+        return gen_mlp_gated(w.M if S is None else S, w.K, w.N, dtype=w.dtype,
+                             amp_x=w.amp_x, amp_w=w.amp_w, seed=w.seed)
     if isinstance(w, MlpWorkload):
         return gen_mlp(w.M if S is None else S, w.K, w.N, dtype=w.dtype,
                        amp_x=w.amp_x, amp_w=w.amp_w, seed=w.seed)

@@ -87,7 +87,8 @@ typedef enum { CHAIN_F32 = 0, CHAIN_BF16 = 1 } chain_dtype;
 typedef enum {
   CHAIN_ACT_GELU_ERF = 0,     /* x * Phi(x) */
   CHAIN_ACT_GELU_TANH = 1,    /* x/2 * (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
-  CHAIN_ACT_IDENTITY = 2
+  CHAIN_ACT_IDENTITY = 2,
+  CHAIN_ACT_SILU = 3          /* x / (1 + exp(-x)) */
 } chain_act;
 
 /* A strided view of device memory.  dtype is a chain_dtype. */
@@ -205,6 +206,30 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1,
 /* Bytes of workspace chain_mlp_fwd needs for an M x N intermediate of dtype
  * dt (a chain_dtype), rounded up to 256.  0 for an invalid dtype. */
 size_t chain_mlp_workspace_bytes(int64_t M, int64_t N, int32_t dt);
+
+/*
+ * chain_mlp_gated_fwd -- O = (act(X.Wg) * (X.Wu)).Wd, * elementwise: the gated MLP
+ * whose gate, up and down projection shards the TSP article circulates ("Lo que
+ * realmente significa plegar"); the activation acts on the gate product only.
+ *
+ *   X      [M, K]    bf16 (input, row-major)
+ *   Wg, Wu [K, N]    bf16 (input), column-major (stride (1, ld)): the transpose of
+ *                    row-major [N, K] weights, as linear layers store them; both
+ *                    with the same strides
+ *   Wd     [N, K2]   bf16 (input), row- or column-major as W2 of chain_mlp_fwd
+ *   O      [M, K2]   bf16 or f32 (output, row-major)
+ *   act    a chain_act (CHAIN_ACT_SILU is the usual gate)
+ *   workspace  as for chain_mlp_fwd: chain_mlp_workspace_bytes(M, N, CHAIN_BF16)
+ *              bytes, 256-byte aligned, holding H = act(X.Wg) * (X.Wu) in bf16
+ *              (rounded to nearest even after the f32 product).
+ * One kernel computes both products of a tile and the gate in its epilogue;
+ * accumulation is f32.  K, N, K2 multiples of 8; f32 inputs or row-major gate/up
+ * weights give CHAIN_ERR_UNSUPPORTED.  Other conventions as chain_mlp_fwd.
+ */
+chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg,
+                                 const chain_tensor *Wu, const chain_tensor *Wd,
+                                 const chain_tensor *O, int act, void *workspace,
+                                 size_t ws_bytes, void *stream);
 
 /*
  * chain_attn_bwd -- gradients of chain_attn_fwd's attention (bf16, whole key

@@ -302,3 +302,36 @@ def test_attn_bwd_validation_codes(lib):
     # Empty sequence: valid, nothing launched.
     t0, _ = _bwd_set(S=0)
     assert _bwd(lib, t0, None, 0) == CODES["CHAIN_OK"]
+
+
+def test_mlp_gated_validation_codes(lib):
+    P = ctypes.byref
+    G = 2 ** 30
+    X = td([512, 256], chain.BF16, FAKE)
+    Wg = td([256, 128], chain.BF16, FAKE + G, stride=[1, 264])        # column-major
+    Wu = td([256, 128], chain.BF16, FAKE + 2 * G, stride=[1, 264])
+    Wd = td([128, 256], chain.BF16, FAKE + 3 * G)
+    O = td([512, 256], chain.BF16, FAKE + 4 * G)
+    need = lib.chain_mlp_workspace_bytes(512, 128, chain.BF16)
+    ws = FAKE + 5 * G
+
+    def call(x=X, wg=Wg, wu=Wu, wd=Wd, o=O, act=3, w=ws, n=need):
+        return lib.chain_mlp_gated_fwd(P(x), P(wg), P(wu), P(wd), P(o), act, w, n, None)
+
+    # everything else valid: the missing workspace is what fails
+    assert call(w=None) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert call(n=need - 1) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert call(act=9, w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    # gate/up weights must be column-major with equal strides
+    assert call(wg=td([256, 128], chain.BF16, FAKE + G), w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    assert call(wu=td([256, 128], chain.BF16, FAKE + 2 * G, stride=[1, 272]), w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    assert call(wu=td([256, 136], chain.BF16, FAKE + 2 * G, stride=[1, 264]), w=None) == CODES["CHAIN_ERR_SHAPE"]
+    assert call(wd=td([128, 256], chain.F32, FAKE + 3 * G), w=None) == CODES["CHAIN_ERR_DTYPE"]
+    f32 = dict(x=td([512, 256], chain.F32, FAKE), wg=td([256, 128], chain.F32, FAKE + G, stride=[1, 264]),
+               wu=td([256, 128], chain.F32, FAKE + 2 * G, stride=[1, 264]), wd=td([128, 256], chain.F32, FAKE + 3 * G))
+    assert call(w=None, **f32) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    assert call(o=td([512, 256], chain.BF16, FAKE + G + 64), w=None) == CODES["CHAIN_ERR_ALIAS"]
+    assert call(w=FAKE + 2 * G + 1024) == CODES["CHAIN_ERR_ALIAS"]
+    assert call(w=ws + 16) == CODES["CHAIN_ERR_ALIGN"]
+    assert call(x=td([512, 250], chain.BF16, FAKE, stride=[256, 1]), wg=td([250, 128], chain.BF16, FAKE + G, stride=[1, 264]),
+                wu=td([250, 128], chain.BF16, FAKE + 2 * G, stride=[1, 264]), w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]

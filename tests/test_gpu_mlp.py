@@ -142,10 +142,11 @@ def test_mlp_empty_inner_dimensions(dtype, kmajor):
         assert torch.all(o == 0), (K, N)
 
 
-@pytest.mark.parametrize("act", ["gelu_erf", "gelu_tanh"])
+@pytest.mark.parametrize("act", ["gelu_erf", "gelu_tanh", "silu"])
 def test_mlp_activation_accuracy_f32(act):
     """X.I.I in f32 isolates the activation: O = act(X) up to its approximation error
-    (the erf form uses a rational approximation with |error| <= 1.5e-7)."""
+    (the erf form uses a rational approximation with |error| <= 1.5e-7; SiLU uses the
+    hardware exp2 and reciprocal, about one ulp each)."""
     dev = device()
     M, N = 512, 64
     z = torch.linspace(-9.0, 9.0, M * N, dtype=torch.float64).reshape(M, N)
@@ -154,7 +155,7 @@ def test_mlp_activation_accuracy_f32(act):
     announce(f"mlp activation accuracy {act}")
     o = chain.mlp_fwd(x.to(dev), eye.to(dev), eye.to(dev), act=act)
     torch.cuda.synchronize()
-    ref = oracle.gelu_erf(f64(x)) if act == "gelu_erf" else oracle.gelu_tanh(f64(x))
+    ref = oracle.ACTIVATIONS[act](f64(x))
     err = np.abs(f64(o) - ref)
     bound = 1e-6 + 2e-7 * np.abs(f64(x))
     print(f"max-abs {err.max():.3e}")
