@@ -26,6 +26,13 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-file extra flags.  attn_bwd.hip: MFMA results in ordinary VGPRs (the
+# softmax of the backward reads every S and dP accumulator with vector ALU ops,
+# and the register allocator otherwise shuffles the dK/dV accumulators between
+# AGPRs and VGPRs around the MFMAs).
+EXTRA = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -33,7 +40,7 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

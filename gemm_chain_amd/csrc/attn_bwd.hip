@@ -24,8 +24,12 @@
 //  - dkdv: four waves (one per SIMD, for the two 32-key accumulators) take 128
 //    keys of one key/value head, 32 per wave with their K and V fragments in
 //    registers, and walk every visible 64-row query tile of every query head of
-//    the group.  Per tile and wave: S = Q.K^T and dP = dO.V^T, P and dS, then
-//    dV^T += dO^T.P and dK^T += Q^T.dS with dO^T and Q^T read transposed.
+//    the group.  Per tile and wave, for its two 32-query halves: S = Q.K^T and
+//    dP = dO.V^T, P and dS, then dV^T += dO^T.P and dK^T += Q^T.dS with dO^T
+//    and Q^T read transposed.  With one wave per SIMD nothing else hides the
+//    softmax, so the wave interleaves it by hand: the second half's S/dP MFMAs
+//    carry the first half's softmax between them, and the first half's dV/dK
+//    MFMAs the second half's.
 // Tiles reach LDS by buffer loads that write LDS directly, into a ring of four
 // stages fetched three tiles ahead, one barrier per tile.  A staged row's
 // 16-byte chunks are XOR-swizzled so that both the 16-byte row-fragment reads
@@ -420,43 +424,84 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
     auto compute = [&](int st_i, int st) {
       if (!wave_keys) return;
       const int q0 = (t0 + st_i % per_head) * QT;
+      if (p.causal && q0 + QT - 1 < kw0) return;   // every query precedes every key
       const char *sb = lds + st * SB;
       const float *rv = (const float *)(sb + 2 * TB);
+      // query q0 + 32qb + 8g + 4h2 + e sees key my_key iff 32qb + 8g + e >= qoff
+      const int qoff = p.causal ? my_key - q0 - 4 * h2 : -(1 << 30);
+      f32x16 s[2], dp[2];
+      bf16x8 pk[2][2], dsk[2][2];
+      f32x4 l4[2][4], d4[2][4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qf0 = q0 + 32 * qb;
-        if (p.causal && qf0 + 31 < kw0) continue;   // every query precedes every key
-        const bool diag = p.causal && qf0 < kw0 + 31;
-        const char *qt_ = sb + qb * 32 * RB;
-        f32x16 s = f32x16{}, dp = f32x16{};
-        run_b128<KS>([&](int i) { return qt_ + fo.aoff[i]; },
-                     [&](int i, bf16x8 a) { s = mfma32(a, kf[i], s); });
-        run_b128<KS>([&](int i) { return qt_ + TB + fo.aoff[i]; },
-                     [&](int i, bf16x8 a) { dp = mfma32(a, vf[i], dp); });
-        // lane (h2, l32) holds query qf0 + 8(r/4) + 4h2 + r%4 of key my_key
-        bf16x8 pk[2], dsk[2];
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ri = rv_index(32 * qb + 8 * g + 4 * h2);
-          const f32x4 l4 = *(const f32x4 *)(rv + ri);
-          const f32x4 d4 = *(const f32x4 *)(rv + ri + 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float x = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[e]));
-            if (diag) x = my_key <= qf0 + 8 * g + 4 * h2 + e ? x : 0.f;
-            pk[r >> 3][r & 7] = (__bf16)x;
-            dsk[r >> 3][r & 7] = (__bf16)(x * (dp[r] - d4[e]));
-          }
+          l4[qb][g] = *(const f32x4 *)(rv + ri);
+          d4[qb][g] = *(const f32x4 *)(rv + ri + 16);
         }
-        // dV^T += dO^T . P and dK^T += Q^T . dS over this block's 32 queries
-        run_tr<2 * DB>([&](int i) { return qt_ + TB + (i & 1) * 16 * RB + fo.tlo[i >> 1]; },
-                       [&](int i) { return qt_ + TB + (i & 1) * 16 * RB + fo.thi[i >> 1]; },
-                       [&](int i, bf16x8 a) { dva[i >> 1] = mfma32(a, pk[i & 1], dva[i >> 1]); });
-        run_tr<2 * DB>([&](int i) { return qt_ + (i & 1) * 16 * RB + fo.tlo[i >> 1]; },
-                       [&](int i) { return qt_ + (i & 1) * 16 * RB + fo.thi[i >> 1]; },
-                       [&](int i, bf16x8 a) { dka[i >> 1] = mfma32(a, dsk[i & 1], dka[i >> 1]); });
-      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[qb] = f32x16{}, dp[qb] = f32x16{};
+      // P and dS of element r (query 8(r/4) + 4h2 + r%4 of the block) of block qb
+      auto elem = [&](int qb, int r) {
+        const int g = r >> 2, e = r & 3;
+        float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l4[qb][g][e]));
+        x = 32 * qb + 8 * g + e >= qoff ? x : 0.f;
+        pk[qb][r >> 3][r & 7] = (__bf16)x;
+        dsk[qb][r >> 3][r & 7] = (__bf16)(x * (dp[qb][r] - d4[qb][g][e]));
+      };
+      constexpr int NM = 2 * KS;          // MFMAs per phase (= 4 * DB)
+      constexpr int EPM = 16 / NM;        // softmax elements per MFMA
+      // MFMA i of S, dP of block qb: even i -> S (A: Q rows), odd i -> dP (A: dO rows)
+      auto sdp = [&](int qb, auto side) {
+        auto addr = [&](int i) { return sb + qb * 32 * RB + ((i & 1) ? TB : 0) + fo.aoff[i >> 1]; };
+        constexpr int A = kAhead;
+        bf16x8 f[A];
+#pragma unroll
+        for (int i = 0; i < A; ++i) f[i] = *(const bf16x8 *)addr(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          const bf16x8 fa = f[i % A];
+          if (i + A < NM) f[i % A] = *(const bf16x8 *)addr(i + A);
+          if (i & 1) dp[qb] = mfma32(fa, vf[i >> 1], dp[qb]);
+          else s[qb] = mfma32(fa, kf[i >> 1], s[qb]);
+          side(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // MFMA i of dV, dK of block qb: column block i / 4, half (i / 2) % 2; even i ->
+      // dV (A: dO^T), odd i -> dK (A: Q^T)
+      auto dvdk = [&](int qb, auto side) {
+        auto lo = [&](int i) { return sb + qb * 32 * RB + ((i & 1) ? 0 : TB) + ((i >> 1) & 1) * 16 * RB + fo.tlo[i >> 2]; };
+        auto hi = [&](int i) { return sb + qb * 32 * RB + ((i & 1) ? 0 : TB) + ((i >> 1) & 1) * 16 * RB + fo.thi[i >> 2]; };
+        constexpr int A = kAhead;
+        i16x4 fl[A], fh[A];
+#pragma unroll
+        for (int i = 0; i < A; ++i) fl[i] = ds_read_tr(lo(i)), fh[i] = ds_read_tr(hi(i));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          const bf16x8 fa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(fl[i % A], fh[i % A], 0, 1, 2, 3, 4, 5, 6, 7));
+          if (i + A < NM) fl[i % A] = ds_read_tr(lo(i + A)), fh[i % A] = ds_read_tr(hi(i + A));
+          const int db = i >> 2, hh = (i >> 1) & 1;
+          if (i & 1) dka[db] = mfma32(fa, dsk[qb][hh], dka[db]);
+          else dva[db] = mfma32(fa, pk[qb][hh], dva[db]);
+          side(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto none = [](int) {};
+      sdp(0, none);
+      sdp(1, [&](int i) {
+#pragma unroll
+        for (int k = 0; k < EPM; ++k) elem(0, i * EPM + k);
+      });
+      dvdk(0, [&](int i) {
+#pragma unroll
+        for (int k = 0; k < EPM; ++k) elem(1, i * EPM + k);
+      });
+      dvdk(1, none);
     };
 
     // Same ring as the dq kernel (steps >= 1: the last query tile sees every key).
