@@ -16,6 +16,9 @@ Sources (cited by page and section; the text of the pages is not quoted):
 * TSP article (7minutos.es, Zyphra TSP), section "Lo que realmente significa
   plegar" -- causal attention over the full, zigzag-reordered K/V context, and
   MLP partial outputs accumulated locally shard by shard.
+* LASP summary (linnk.ai), abstract -- linear attention parallelised over the
+  sequence by passing an intermediate key/value state between devices; the
+  right-product trick and KV-state caching.
 * 2D-Attention summary (scisimple.com), sections "Introduciendo la Atencion 2D"
   (tensors chunked along the context dimension) and "Comprendiendo la
   Arquitectura de los LLMs" (MHA; GQA query heads sharing one K/V head set).
@@ -27,6 +30,7 @@ Modules:
   mlp       -- act(X.W1).W2 with erf-GeLU, tanh-GeLU, SiLU or identity, and the
                gated form (act(X.Wg) * (X.Wu)).Wd
   zigzag    -- zigzag shares and chunks of a sequence; visible-pair counts
+  linear_attention -- causal linear attention with a carried key/value state (LASP)
   brute     -- element-by-element loops (math.fsum / math.exp) for tiny cases
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
@@ -39,6 +43,7 @@ from .attention import attention, attention_rows, visible_mask
 from .attention_bwd import attention_bwd, attention_bwd_loss
 from .merge import lse_merge
 from .mlp import gelu_erf, gelu_tanh, silu, mlp, mlp_gated, ACTIVATIONS
+from .linear_attention import linear_attention, linear_attention_chunked
 from .zigzag import (natural_chunk_positions, zigzag_chunk_positions,
                      zigzag_share_positions, visible_pairs)
 
@@ -46,4 +51,5 @@ __all__ = [
     "attention", "attention_rows", "visible_mask", "attention_bwd", "attention_bwd_loss", "lse_merge", "gelu_erf",
     "gelu_tanh", "silu", "mlp", "mlp_gated", "ACTIVATIONS", "natural_chunk_positions",
     "zigzag_chunk_positions", "zigzag_share_positions", "visible_pairs",
+    "linear_attention", "linear_attention_chunked",
 ]

@@ -80,3 +80,29 @@ def mlp_gated(x, wg, wu, wd, form="silu"):
           math.fsum(x[i][kk] * wu[kk][n] for kk in range(K)) for n in range(N)] for i in range(M)]
     return [[math.fsum(H[i][n] * wd[n][c] for n in range(N)) for c in range(K2)]
             for i in range(M)]
+
+
+def linear_attention(q, k, v, s_in=None):
+    """Causal linear attention with a carried state, element by element:
+    O[b,h,i,e] = fsum_{j<=i} (fsum_d q k) v[j,e] + fsum_d q[i,d] s_in[d,e];
+    S_out[b,g,d,e] = s_in[d,e] + fsum_j k[j,d] v[j,e]."""
+    q, k, v = _tolist(q), _tolist(k), _tolist(v)
+    B, Hq, S, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv = len(k[0])
+    group = Hq // Hkv
+    if s_in is None:
+        s_in = [[[[0.0] * D for _ in range(D)] for _ in range(Hkv)] for _ in range(B)]
+    else:
+        s_in = _tolist(s_in)
+    o = [[[[0.0] * D for _ in range(S)] for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for i in range(S):
+                sc = [math.fsum(q[b][h][i][d] * k[b][g][j][d] for d in range(D)) for j in range(i + 1)]
+                for e in range(D):
+                    o[b][h][i][e] = math.fsum([sc[j] * v[b][g][j][e] for j in range(i + 1)] +
+                                              [q[b][h][i][d] * s_in[b][g][d][e] for d in range(D)])
+    s_out = [[[[math.fsum([s_in[b][g][d][e]] + [k[b][g][j][d] * v[b][g][j][e] for j in range(S)])
+                for e in range(D)] for d in range(D)] for g in range(Hkv)] for b in range(B)]
+    return o, s_out

@@ -305,6 +305,48 @@ def check_mlp_gated(mlp_gated, mlp, brute):
     assert np.max(np.abs(parts - full)) <= 1e-13
 
 
+# --------------------------------------------------------- linear attention
+
+def check_linear_attention(lin, lin_chunked, brute):
+    rng = np.random.default_rng(21)
+    # brute force on tiny shapes, GQA 2:1, with a carried state
+    q = rng.standard_normal((1, 2, 5, 3))
+    k = rng.standard_normal((1, 1, 5, 3))
+    v = rng.standard_normal((1, 1, 5, 3))
+    s_in = rng.standard_normal((1, 1, 3, 3))
+    o, so = lin(q, k, v, s_in)
+    ob, sob = brute.linear_attention(q, k, v, s_in)
+    assert np.max(np.abs(o - np.array(ob))) <= 1e-13
+    assert np.max(np.abs(so - np.array(sob))) <= 1e-13
+    # the right-product chunk recurrence equals the definition (ragged last chunk)
+    q = rng.standard_normal((2, 4, 37, 8))
+    k = rng.standard_normal((2, 2, 37, 8))
+    v = rng.standard_normal((2, 2, 37, 8))
+    s_in = rng.standard_normal((2, 2, 8, 8))
+    o, so = lin(q, k, v, s_in)
+    for chunk in (1, 5, 16, 37, 64):
+        oc, soc = lin_chunked(q, k, v, chunk, s_in)
+        assert np.max(np.abs(oc - o)) <= 1e-11 and np.max(np.abs(soc - so)) <= 1e-11
+    # state passing: the second share with the first share's state continues the sequence
+    o1, s1 = lin(q[:, :, :20], k[:, :, :20], v[:, :, :20], s_in)
+    o2, s2 = lin(q[:, :, 20:], k[:, :, 20:], v[:, :, 20:], s1)
+    assert np.max(np.abs(np.concatenate([o1, o2], axis=2) - o)) <= 1e-11
+    assert np.max(np.abs(s2 - so)) <= 1e-11
+    # closed forms: V = 1 gives every column q_i . sum_{j<=i} k_j; K = 0 gives Q S_in
+    ones = np.ones_like(v)
+    o, _ = lin(q, k, ones)
+    pref = np.cumsum(np.repeat(k, 2, axis=1), axis=2)
+    expect = np.einsum("bhid,bhid->bhi", q, pref)
+    assert np.max(np.abs(o - expect[..., None])) <= 1e-11
+    o, so = lin(q, np.zeros_like(k), v, s_in)
+    assert np.max(np.abs(o - np.einsum("bhid,bhde->bhie", q, np.repeat(s_in, 2, axis=1)))) <= 1e-12
+    assert np.array_equal(so, s_in)
+    # row 0 sees only key 0: O_0 = (q_0 . k_0) v_0 without a state
+    o, _ = lin(q, k, v)
+    r0 = np.einsum("bhd,bhd->bh", q[:, :, 0], np.repeat(k[:, :, 0], 2, axis=1))[..., None] * np.repeat(v[:, :, 0], 2, axis=1)
+    assert np.max(np.abs(o[:, :, 0] - r0)) <= 1e-12
+
+
 # -------------------------------------------------------------------- zigzag
 
 def check_zigzag(zigzag_share_positions, visible_pairs):

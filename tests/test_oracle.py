@@ -82,3 +82,7 @@ def test_silu_closed_forms_and_identities():
 
 def test_gated_mlp_brute_force_reductions_and_shards():
     P.check_mlp_gated(oracle.mlp_gated, oracle.mlp, brute)
+
+
+def test_linear_attention_brute_chunked_state_passing_and_closed_forms():
+    P.check_linear_attention(oracle.linear_attention, oracle.linear_attention_chunked, brute)

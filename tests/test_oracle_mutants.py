@@ -194,3 +194,32 @@ def test_gated_mlp_mutants_caught():
 
     for bad in (act_on_up, no_act, added):
         assert _count_failures([lambda: P.check_mlp_gated(bad, oracle.mlp, brute)]) == 1
+
+
+def test_linear_attention_mutants_caught():
+    """A strict mask, a dropped carried state, a transposed state, and a state
+    that forgets S_in: each must fail a pin."""
+    OL = importlib.import_module("oracle.linear_attention")
+
+    def make(kind):
+        def lin(q, k, v, s_in=None):
+            q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+            B, Hq, S, D = q.shape
+            Hkv = k.shape[1]
+            g = Hq // Hkv
+            s0 = np.zeros((B, Hkv, D, D)) if s_in is None else np.asarray(s_in, dtype=np.float64)
+            mask = np.tril(np.ones((S, S)), -1 if kind == "strict" else 0)
+            st = s0.transpose(0, 1, 3, 2) if kind == "transposed" else s0
+            o = np.zeros_like(q)
+            for b in range(B):
+                for h in range(Hq):
+                    o[b, h] = ((q[b, h] @ k[b, h // g].T) * mask) @ v[b, h // g]
+                    if kind != "no_state":
+                        o[b, h] += q[b, h] @ st[b, h // g]
+            kv = np.einsum("bgjd,bgje->bgde", k, v)
+            return o, (kv if kind == "forget" else s0 + kv)
+        return lin
+
+    for kind in ("strict", "no_state", "transposed", "forget"):
+        bad = make(kind)
+        assert _count_failures([lambda: P.check_linear_attention(bad, OL.linear_attention_chunked, brute)]) == 1, kind
