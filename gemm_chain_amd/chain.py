@@ -73,6 +73,8 @@ def load():
         "chain_mlp_gated_fwd": (ctypes.c_int, [T, T, T, T, T, ctypes.c_int, vp, sz, vp]),
         "chain_attn_bwd": (ctypes.c_int, [T, T, T, T, T, T, T, T, T, ctypes.c_int, f32, vp, sz, vp]),
         "chain_attn_bwd_workspace_bytes": (sz, [i64, i64, i64]),
+        "chain_linear_attn_fwd": (ctypes.c_int, [T, T, T, T, T, T, vp, sz, vp]),
+        "chain_linear_attn_workspace_bytes": (sz, [i64, i64, i64, i64]),
         "chain_zigzag_segs": (ctypes.c_int, [i64, i32, i32, S]),
         "chain_attn_tile_census": (ctypes.c_int, [i64, S, i64, S, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -186,6 +188,30 @@ def attn_bwd(q, k, v, o, lse, do, causal=True, scale=None, dq=None, dk=None, dv=
                               ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                               _stream(q)))
     return dq, dk, dv
+
+
+def linear_attn_workspace_bytes(B, Hkv, S, D):
+    return int(load().chain_linear_attn_workspace_bytes(int(B), int(Hkv), int(S), int(D)))
+
+
+def linear_attn_fwd(q, k, v, s_in=None, want_state=True, out=None, out_dtype=torch.float32,
+                    s_out=None, workspace=None):
+    """(O, S_out) of causal linear attention carrying the state s_in (None: zero)."""
+    lib = load()
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    o = torch.empty((B, Hq, S, D), dtype=out_dtype, device=q.device) if out is None else out
+    so = s_out
+    if so is None and want_state:
+        so = torch.empty((B, Hkv, D, D), dtype=torch.float32, device=q.device)
+    need = linear_attn_workspace_bytes(B, Hkv, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.chain_linear_attn_fwd(desc(q), desc(k), desc(v), desc(o),
+                                     desc(s_in) if s_in is not None else None,
+                                     desc(so) if so is not None else None,
+                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(q)))
+    return o, so
 
 
 def mlp_workspace_bytes(M, N, dtype=torch.bfloat16):

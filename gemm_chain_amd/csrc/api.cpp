@@ -522,6 +522,80 @@ chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg, 
   return ok();
 }
 
+size_t chain_linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D) {
+  if (B < 0 || Hkv < 0 || S < 0 || D < 0) return 0;
+  return chain::linear_attn_workspace_bytes(B, Hkv, S, D);
+}
+
+chain_status chain_linear_attn_fwd(const chain_tensor *Q, const chain_tensor *K, const chain_tensor *V,
+                                   const chain_tensor *O, const chain_tensor *S_in, const chain_tensor *S_out,
+                                   void *workspace, size_t ws_bytes, void *stream) {
+  TRY(check_tensor(Q, "Q", 4));
+  TRY(check_tensor(K, "K", 4));
+  TRY(check_tensor(V, "V", 4));
+  TRY(check_tensor(O, "O", 4));
+  if (S_in) TRY(check_tensor(S_in, "S_in", 4, 4));
+  if (S_out) TRY(check_tensor(S_out, "S_out", 4, 4));
+  if (Q->dtype != CHAIN_BF16 || K->dtype != CHAIN_BF16 || V->dtype != CHAIN_BF16)
+    return fail(CHAIN_ERR_DTYPE, "Q, K and V must be bf16");
+  if ((S_in && S_in->dtype != CHAIN_F32) || (S_out && S_out->dtype != CHAIN_F32))
+    return fail(CHAIN_ERR_DTYPE, "states must be f32");
+  const int64_t B = Q->shape[0], Hq = Q->shape[1], S = Q->shape[2], D = Q->shape[3];
+  for (int i = 0; i < 4; ++i) {
+    if (K->shape[i] != V->shape[i]) return fail(CHAIN_ERR_SHAPE, "K and V shapes differ");
+    if (O->shape[i] != Q->shape[i]) return fail(CHAIN_ERR_SHAPE, "O shape must equal Q shape");
+  }
+  if (K->shape[0] != B || K->shape[2] != S || K->shape[3] != D)
+    return fail(CHAIN_ERR_SHAPE, "K/V must be [B, Hkv, S, D] with Q's B, S and D");
+  const int64_t Hkv = K->shape[1];
+  if (Hkv == 0 ? Hq != 0 : Hq % Hkv != 0)
+    return fail(CHAIN_ERR_SHAPE, "query heads must be a multiple of key/value heads");
+  for (const chain_tensor *st : {S_in, S_out})
+    if (st && (st->shape[0] != B || st->shape[1] != Hkv || st->shape[2] != D || st->shape[3] != D))
+      return fail(CHAIN_ERR_SHAPE, "states must be [B, Hkv, D, D]");
+  if (D != 64 && D != 128) return fail(CHAIN_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)D);
+  if (S > INT32_MAX / 2 || B * Hq * ((S + 127) / 128) > INT32_MAX || B * Hkv * 16 > INT32_MAX)
+    return fail(CHAIN_ERR_UNSUPPORTED, "sizes too large");
+  const chain_tensor *ins[] = {Q, K, V, S_in};
+  for (const chain_tensor *t : ins)
+    if (t && (overlap(*O, *t) || (S_out && overlap(*S_out, *t))))
+      return fail(CHAIN_ERR_ALIAS, "outputs overlap inputs or each other");
+  if (S_out && overlap(*S_out, *O)) return fail(CHAIN_ERR_ALIAS, "outputs overlap inputs or each other");
+  if (B == 0 || Hkv == 0) return ok();
+  const size_t need = chain::linear_attn_workspace_bytes(B, Hkv, S, D);
+  if (S > 0) {
+    if (workspace == nullptr || ws_bytes < need)
+      return fail(CHAIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    if ((uintptr_t)workspace % 256) return fail(CHAIN_ERR_ALIGN, "workspace must be 256-byte aligned");
+    chain_tensor W{};
+    W.data = workspace;
+    W.dtype = CHAIN_F32;
+    W.ndim = 1;
+    W.shape[0] = (int64_t)(need / 4);
+    W.stride[0] = 1;
+    for (const chain_tensor *t : {Q, K, V, O, S_in, S_out})
+      if (t && overlap(W, *t)) return fail(CHAIN_ERR_ALIAS, "workspace overlaps a tensor");
+  }
+  chain::LinAttnParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = Q->data, p.k = K->data, p.v = V->data, p.o = O->data;
+  p.s_in = S_in ? (const float *)S_in->data : nullptr;
+  p.s_out = S_out ? (float *)S_out->data : nullptr;
+  p.delta = (float *)workspace;
+  p.pref = workspace ? (__bf16 *)((char *)workspace + chain::linear_attn_pref_offset(B, Hkv, S, D)) : nullptr;
+  p.q_sb = Q->stride[0], p.q_sh = Q->stride[1], p.q_ss = Q->stride[2];
+  p.k_sb = K->stride[0], p.k_sh = K->stride[1], p.k_ss = K->stride[2];
+  p.v_sb = V->stride[0], p.v_sh = V->stride[1], p.v_ss = V->stride[2];
+  p.o_sb = O->stride[0], p.o_sh = O->stride[1], p.o_ss = O->stride[2];
+  if (S_in) p.si_sb = S_in->stride[0], p.si_sh = S_in->stride[1], p.si_sr = S_in->stride[2];
+  if (S_out) p.so_sb = S_out->stride[0], p.so_sh = S_out->stride[1], p.so_sr = S_out->stride[2];
+  p.B = (int32_t)B, p.Hq = (int32_t)Hq, p.Hkv = (int32_t)Hkv, p.S = (int32_t)S;
+  p.o_f32 = O->dtype == CHAIN_F32;
+  hipError_t e = chain::launch_linear_attn(p, (int)D, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CHAIN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 chain_status chain_zigzag_segs(int64_t S, int32_t parts, int32_t r, chain_segs *out) {
   if (out == nullptr) return fail(CHAIN_ERR_NULL, "out is NULL");
   if (parts < 1 || S <= 0 || S % (2 * (int64_t)parts))

@@ -190,11 +190,31 @@ struct AttnBwdParams {
   float scale_log2;   // scale * log2(e)
 };
 
+struct LinAttnParams {
+  const void *q, *k, *v;              // bf16 [B, Hq|Hkv, S, D]
+  void *o;                            // [B, Hq, S, D], f32 or bf16
+  const float *s_in;                  // [B, Hkv, D_k, D_v] or null (zero state)
+  float *s_out;                       // [B, Hkv, D_k, D_v] or null
+  float *delta;                       // workspace: per chunk K_t^T V_t, transposed, f32
+  __bf16 *pref;                       // workspace: state before each chunk, transposed, bf16
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t si_sb, si_sh, si_sr;
+  int64_t so_sb, so_sh, so_sr;
+  int32_t B, Hq, Hkv, S;
+  int32_t o_f32;
+};
+
 // Launchers (defined in the .hip files).  Each returns the launch's hipError_t.
 hipError_t launch_attn_mfma_bf16(const AttnParams &p, int D, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnBwdParams &p, int D, hipStream_t stream);
+hipError_t launch_linear_attn(const LinAttnParams &p, int D, hipStream_t stream);
+size_t linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D);
+size_t linear_attn_pref_offset(int64_t B, int64_t Hkv, int64_t S, int64_t D);
 
 }  // namespace chain

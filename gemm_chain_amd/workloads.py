@@ -73,6 +73,10 @@ WORKLOADS = {
     "mlp_gated_bf16_m16384_k4096_n1376": MlpWorkload(
         "mlp_gated_bf16_m16384_k4096_n1376", "bf16", 16384, 4096, 1376, 1.0, 0.02, 6, act="silu",
         gated=True),
+    # one device's share (32768 tokens, e.g. 4096K tokens over 128 devices) of causal
+    # linear attention with a carried key/value state, 32 heads of 128
+    "lin_attn_bf16_h32_s32768_d128": AttnWorkload(
+        "lin_attn_bf16_h32_s32768_d128", "bf16", 1, 32, 32, 32768, 128, 0.25, 7),
     # long causal GQA attention, 32 query heads over 8 KV heads, 16 zigzag chunks
     "attn_gqa_bf16_h32kv8_s65536_d128": AttnWorkload(
         "attn_gqa_bf16_h32kv8_s65536_d128", "bf16", 1, 32, 8, 65536, 128, 1.0, 5,
@@ -94,6 +98,12 @@ def gen_attention_grad(B, Hq, S, D, dtype="bf16", amp=1.0, seed=0):
     """dO [B,Hq,S,D] on the CPU: the output gradient fed to the attention backward."""
     g = torch.Generator().manual_seed(seed)
     return (torch.randn(B, Hq, S, D, generator=g, dtype=torch.float32) * amp).to(_DTYPES[dtype])
+
+
+def gen_linear_state(B, Hkv, D, amp=1.0, seed=0):
+    """A carried key/value state S_in [B,Hkv,D,D] in f32 on the CPU (N(0, amp^2))."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(B, Hkv, D, D, generator=g, dtype=torch.float32) * amp
 
 
 def gen_mlp(M, K, N, K2=None, dtype="bf16", amp_x=1.0, amp_w=0.02, seed=0):

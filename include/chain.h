@@ -271,6 +271,39 @@ chain_status chain_attn_bwd(const chain_tensor *Q, const chain_tensor *K, const 
 size_t chain_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t S);
 
 /*
+ * chain_linear_attn_fwd -- causal linear attention with a carried key/value state:
+ * one device's share of linear-attention sequence parallelism (LASP summary,
+ * abstract: an intermediate key/value state is handed from device to device;
+ * right-product evaluation; the intermediate states are cached).  With no
+ * normalisation and no decay (the page prints no formula), for query head h and
+ * key/value head g = h / (Hq / Hkv):
+ *   O_i   = sum_{j<=i} (q_i . k_j) v_j + q_i S_in,
+ *   S_out = S_in + sum_j k_j^T v_j          (D x D, row d_k, column d_v)
+ *
+ *   Q      [B, Hq, S, D]    bf16 (input)
+ *   K, V   [B, Hkv, S, D]   bf16 (input), Hq % Hkv == 0
+ *   O      [B, Hq, S, D]    f32 or bf16 (output)
+ *   S_in   [B, Hkv, D, D]   f32 (input; NULL = zero state, the first share)
+ *   S_out  [B, Hkv, D, D]   f32 (output; NULL to skip)
+ *   workspace  at least chain_linear_attn_workspace_bytes(B, Hkv, S, D) bytes,
+ *              256-byte aligned; caller-owned scratch holding, per 128-row chunk,
+ *              K_t^T V_t (f32) and the state before the chunk (bf16, the second
+ *              product's MFMA operand)
+ * Products are bf16 MFMAs with f32 accumulation; the in-chunk scores are rounded
+ * to bf16 as an MFMA operand.  D must be 64 or 128.  The last dimension of every
+ * tensor is contiguous; Q, K, V, O 16-byte aligned, the states 4-byte aligned.
+ * S == 0 is valid (S_out = S_in).  Outputs and workspace must not overlap inputs
+ * or each other.
+ */
+chain_status chain_linear_attn_fwd(const chain_tensor *Q, const chain_tensor *K,
+                                   const chain_tensor *V, const chain_tensor *O,
+                                   const chain_tensor *S_in, const chain_tensor *S_out,
+                                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace chain_linear_attn_fwd needs (0 for negative sizes). */
+size_t chain_linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D);
+
+/*
  * chain_zigzag_segs -- host helper: the positions of share r of `parts` in a
  * zigzag split of S tokens (TSP article, zigzag partition): the pieces r and
  * 2*parts-1-r of 2*parts equal pieces, as two runs in ascending order.  Used

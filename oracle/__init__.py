@@ -43,7 +43,7 @@ from .attention import attention, attention_rows, visible_mask
 from .attention_bwd import attention_bwd, attention_bwd_loss
 from .merge import lse_merge
 from .mlp import gelu_erf, gelu_tanh, silu, mlp, mlp_gated, ACTIVATIONS
-from .linear_attention import linear_attention, linear_attention_chunked
+from .linear_attention import linear_attention, linear_attention_chunked, linear_attention_rows
 from .zigzag import (natural_chunk_positions, zigzag_chunk_positions,
                      zigzag_share_positions, visible_pairs)
 
@@ -51,5 +51,5 @@ __all__ = [
     "attention", "attention_rows", "visible_mask", "attention_bwd", "attention_bwd_loss", "lse_merge", "gelu_erf",
     "gelu_tanh", "silu", "mlp", "mlp_gated", "ACTIVATIONS", "natural_chunk_positions",
     "zigzag_chunk_positions", "zigzag_share_positions", "visible_pairs",
-    "linear_attention", "linear_attention_chunked",
+    "linear_attention", "linear_attention_chunked", "linear_attention_rows",
 ]

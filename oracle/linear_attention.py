@@ -73,3 +73,22 @@ def linear_attention_chunked(q, k, v, chunk, s_in=None):
                 o[b, h, t0:t1] = ((qt @ kt.T) * m) @ vt + qt @ state[b, g]
         state = state + np.einsum("bgjd,bgje->bgde", k[:, :, t0:t1], v[:, :, t0:t1])
     return o, state
+
+
+def linear_attention_rows(q, k, v, rows, s_in=None):
+    """O at the given query rows only, by the definition (each row against its
+    key prefix): [B, Hq, len(rows), D] in float64.  For checks at sizes where the
+    full S x S score matrix does not fit."""
+    q, k, v = _widen(q, k, v)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    s_in = np.zeros((B, Hkv, D, D)) if s_in is None else np.asarray(s_in, dtype=np.float64)
+    out = np.zeros((B, Hq, len(rows), D))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for n, i in enumerate(rows):
+                sc = k[b, g, :i + 1] @ q[b, h, i]
+                out[b, h, n] = sc @ v[b, g, :i + 1] + q[b, h, i] @ s_in[b, g]
+    return out

@@ -307,7 +307,8 @@ def check_mlp_gated(mlp_gated, mlp, brute):
 
 # --------------------------------------------------------- linear attention
 
-def check_linear_attention(lin, lin_chunked, brute):
+def check_linear_attention(lin, lin_chunked, brute, lin_rows=None):
+    OLR = lin_rows if lin_rows is not None else (lambda q, k, v, rows, s: lin(q, k, v, s)[0][:, :, rows])
     rng = np.random.default_rng(21)
     # brute force on tiny shapes, GQA 2:1, with a carried state
     q = rng.standard_normal((1, 2, 5, 3))
@@ -341,6 +342,10 @@ def check_linear_attention(lin, lin_chunked, brute):
     o, so = lin(q, np.zeros_like(k), v, s_in)
     assert np.max(np.abs(o - np.einsum("bhid,bhde->bhie", q, np.repeat(s_in, 2, axis=1)))) <= 1e-12
     assert np.array_equal(so, s_in)
+    # selected rows by the definition agree with the full evaluation
+    rows = [0, 5, 36]
+    o_full, _ = lin(q, k, v, s_in)
+    assert np.max(np.abs(OLR(q, k, v, rows, s_in) - o_full[:, :, rows])) <= 1e-11
     # row 0 sees only key 0: O_0 = (q_0 . k_0) v_0 without a state
     o, _ = lin(q, k, v)
     r0 = np.einsum("bhd,bhd->bh", q[:, :, 0], np.repeat(k[:, :, 0], 2, axis=1))[..., None] * np.repeat(v[:, :, 0], 2, axis=1)

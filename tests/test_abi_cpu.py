@@ -335,3 +335,43 @@ def test_mlp_gated_validation_codes(lib):
     assert call(w=ws + 16) == CODES["CHAIN_ERR_ALIGN"]
     assert call(x=td([512, 250], chain.BF16, FAKE, stride=[256, 1]), wg=td([250, 128], chain.BF16, FAKE + G, stride=[1, 264]),
                 wu=td([250, 128], chain.BF16, FAKE + 2 * G, stride=[1, 264]), w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+
+
+def test_linear_attn_validation_codes(lib):
+    P = ctypes.byref
+    G = 2 ** 30
+    Q = td([1, 4, 256, 128], chain.BF16, FAKE)
+    K = td([1, 2, 256, 128], chain.BF16, FAKE + G)
+    V = td([1, 2, 256, 128], chain.BF16, FAKE + 2 * G)
+    O = td([1, 4, 256, 128], chain.F32, FAKE + 3 * G)
+    Si = td([1, 2, 128, 128], chain.F32, FAKE + 4 * G)
+    So = td([1, 2, 128, 128], chain.F32, FAKE + 5 * G)
+    need = lib.chain_linear_attn_workspace_bytes(1, 2, 256, 128)
+    assert need == 2 * 2 * 128 * 128 * 6     # two chunks: f32 deltas + bf16 states
+    ws = FAKE + 6 * G
+
+    def call(q=Q, k=K, v=V, o=O, si=Si, so=So, w=ws, n=need):
+        return lib.chain_linear_attn_fwd(P(q), P(k), P(v), P(o), P(si) if si else None,
+                                         P(so) if so else None, w, n, None)
+
+    assert call(w=None) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert call(n=need - 1) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert call(w=ws + 64) == CODES["CHAIN_ERR_ALIGN"]
+    assert call(w=FAKE + 2 * G + 4096) == CODES["CHAIN_ERR_ALIAS"]
+    assert call(si=None, so=None, w=None) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert call(q=td([1, 4, 256, 128], chain.F32, FAKE), w=None) == CODES["CHAIN_ERR_DTYPE"]
+    assert call(si=td([1, 2, 128, 128], chain.BF16, FAKE + 4 * G), w=None) == CODES["CHAIN_ERR_DTYPE"]
+    assert call(so=td([1, 2, 128, 64], chain.F32, FAKE + 5 * G), w=None) == CODES["CHAIN_ERR_SHAPE"]
+    assert call(k=td([1, 3, 256, 128], chain.BF16, FAKE + G), v=td([1, 3, 256, 128], chain.BF16, FAKE + 2 * G),
+                w=None) == CODES["CHAIN_ERR_SHAPE"]
+    assert call(o=td([1, 4, 255, 128], chain.F32, FAKE + 3 * G), w=None) == CODES["CHAIN_ERR_SHAPE"]
+    assert call(so=td([1, 2, 128, 128], chain.F32, FAKE + 3 * G + 4096), w=None) == CODES["CHAIN_ERR_ALIAS"]
+    D96 = dict(q=td([1, 4, 256, 96], chain.BF16, FAKE), k=td([1, 2, 256, 96], chain.BF16, FAKE + G),
+               v=td([1, 2, 256, 96], chain.BF16, FAKE + 2 * G), o=td([1, 4, 256, 96], chain.F32, FAKE + 3 * G),
+               si=None, so=None, w=None)
+    assert call(**D96) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    # zero rows with no state to pass: nothing to do
+    E = dict(q=td([1, 4, 0, 128], chain.BF16, FAKE), k=td([1, 2, 0, 128], chain.BF16, FAKE + G),
+             v=td([1, 2, 0, 128], chain.BF16, FAKE + 2 * G), o=td([1, 4, 0, 128], chain.F32, FAKE + 3 * G),
+             si=None, so=None, w=None, n=0)
+    assert call(**E) == CODES["CHAIN_OK"]

@@ -1,0 +1,150 @@
+"""GPU parity of chain_linear_attn_fwd (causal linear attention with a carried
+key/value state) against the float64 oracle.
+
+Tolerance, element by element, from where the kernels round (Q, K, V and S_in
+are the same values on both sides): the in-chunk scores q_i . k_j are rounded
+to bf16 as an MFMA operand, and so is the state before each 128-row chunk;
+everything else accumulates in f32.  So |error of O_ie| is at most
+eps * (sum_{j in chunk, j<=i} |s_ij| |v_je| + sum_d |q_id| |S_de|) plus the f32
+accumulation, bounded by 2^-14 times the same sums with the state's own terms
+spelled out (sum_d |q_id| sum_{j<chunk} |k_jd| |v_je|), with eps = 2^-8 (twice
+bf16's unit roundoff), and doubled for second-order terms.  The relative
+Frobenius error is also held to 2^-7.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_chain_amd import chain
+from gemm_chain_amd.workloads import WORKLOADS, gen_attention, gen_linear_state
+from gpu_util import announce, device, f64, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+EPS = 2.0 ** -8
+ACC = 2.0 ** -14
+CHUNK = 128
+
+
+def _bound(q, k, v, s_in):
+    """Elementwise bound on |O_gpu - O_exact| for the kernels' rounding points."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    s0 = np.zeros((B, Hkv, D, D)) if s_in is None else s_in
+    bound = np.zeros(q.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            state = s0[b, g].copy()
+            astate = np.abs(s0[b, g]).copy()       # the state's terms in absolute value
+            for t0 in range(0, S, CHUNK):
+                t1 = min(t0 + CHUNK, S)
+                qa, ka, va = np.abs(q[b, h, t0:t1]), k[b, g, t0:t1], v[b, g, t0:t1]
+                sc = np.abs(q[b, h, t0:t1] @ ka.T) * np.tril(np.ones((t1 - t0, t1 - t0)))
+                intra = sc @ np.abs(va)
+                inter = qa @ np.abs(state)
+                bound[b, h, t0:t1] = 2 * (EPS * (intra + inter) + ACC * (intra + qa @ astate))
+                state += ka.T @ va
+                astate += np.abs(ka).T @ np.abs(va)
+    return bound
+
+
+def _check(name, got, ref, bound):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), f"{name}: non-finite output"
+    err = np.abs(got - ref)
+    floor = 1e-6 * max(1.0, float(np.abs(ref).max()))
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
+    print(f"{name}: max-abs {err.max():.3e}  max|ref| {np.abs(ref).max():.3e}  "
+          f"err/bound {float((err / (bound + floor)).max()):.3f}  rel-fro {rel:.2e}")
+    assert np.all(err <= bound + floor), f"{name}: error above the derived bound"
+    assert rel <= 2.0 ** -7, f"{name}: relative error {rel:.2e}"
+
+
+CASES = [
+    # B, Hq, Hkv, S, D, with a carried state
+    (1, 4, 4, 300, 128, True),     # ragged last chunk
+    (2, 8, 2, 256, 64, False),     # GQA 4:1, D 64, whole chunks
+    (1, 3, 1, 700, 128, True),     # GQA 3:1, six chunks
+    (1, 2, 2, 129, 64, True),      # one row past a chunk
+    (1, 2, 1, 1, 128, True),       # a single token
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,with_state", CASES)
+def test_linear_attention_small_full_compare(B, Hq, Hkv, S, D, with_state):
+    dev = device()
+    q, k, v = gen_attention(B, Hq, Hkv, S, S, D, "bf16", 0.5, 500 + S)
+    s_in = gen_linear_state(B, Hkv, D, 2.0, 600 + S) if with_state else None
+    announce(f"linear_attn B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} state{int(with_state)}")
+    o, so = chain.linear_attn_fwd(q.to(dev), k.to(dev), v.to(dev),
+                                  s_in=s_in.to(dev) if with_state else None)
+    torch.cuda.synchronize()
+    sn = f64(s_in) if with_state else None
+    ro, rs = oracle.linear_attention(f64(q), f64(k), f64(v), sn)
+    _check("O", f64(o), ro, _bound(f64(q), f64(k), f64(v), sn))
+    # the state: f32 sums of exact bf16 products
+    kv_abs = np.einsum("bgjd,bgje->bgde", np.abs(f64(k)), np.abs(f64(v)))
+    serr = np.abs(f64(so) - rs)
+    print(f"S_out: max-abs {serr.max():.3e}")
+    assert np.all(serr <= ACC * (kv_abs + (np.abs(sn) if with_state else 0)) + 1e-6)
+
+
+def test_linear_attention_state_passing_between_shares():
+    """Two shares with the first's S_out as the second's S_in continue the sequence."""
+    dev = device()
+    B, H, S, D = 1, 4, 640, 128
+    q, k, v = (t.to(dev) for t in gen_attention(B, H, H, S, S, D, "bf16", 0.5, 31))
+    s_in = gen_linear_state(B, H, D, 1.0, 32).to(dev)
+    announce("linear_attn state passing")
+    whole, s_whole = chain.linear_attn_fwd(q, k, v, s_in=s_in)
+    cut = 256
+    o1, s1 = chain.linear_attn_fwd(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], s_in=s_in)
+    o2, s2 = chain.linear_attn_fwd(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], s_in=s1)
+    torch.cuda.synchronize()
+    # the first share is the same computation; the second differs only by where
+    # the state is rounded, so it is held to the oracle bound like the whole
+    assert torch.equal(o1, whole[:, :, :cut])
+    ro, rs = oracle.linear_attention(f64(q), f64(k), f64(v), f64(s_in))
+    _check("O second share", f64(o2), ro[:, :, cut:], _bound(f64(q), f64(k), f64(v), f64(s_in))[:, :, cut:])
+    assert np.max(np.abs(f64(s2) - rs)) <= 1e-3 * np.abs(rs).max()
+
+
+def test_linear_attention_empty_sequence_passes_the_state():
+    dev = device()
+    s_in = gen_linear_state(2, 2, 64, 1.0, 33).to(dev)
+    q = torch.empty(2, 4, 0, 64, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(2, 2, 0, 64, dtype=torch.bfloat16, device=dev)
+    announce("linear_attn S = 0")
+    o, so = chain.linear_attn_fwd(q, k, k.clone(), s_in=s_in)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(so, s_in)
+
+
+def test_linear_attention_full_size_sampled_rows():
+    """One device's 32768-token share, 32 heads of 128: sampled rows of four heads
+    against the definition, and the whole state."""
+    w = WORKLOADS["lin_attn_bf16_h32_s32768_d128"]
+    dev = device()
+    q, k, v = gen_attention(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.amp, w.seed)
+    s_in = gen_linear_state(w.B, w.Hkv, w.D, 1.0, w.seed + 1)
+    announce("linear_attn 1x32x32768x128 full size")
+    o, so = chain.linear_attn_fwd(q.to(dev), k.to(dev), v.to(dev), s_in=s_in.to(dev))
+    torch.cuda.synchronize()
+    rows = sample_rows(w.S, 48, w.seed, extra=(127, 128, 129, 16383, 16384))
+    heads = slice(8, 12)
+    qn, kn, vn, sn = f64(q[:, heads]), f64(k[:, heads]), f64(v[:, heads]), f64(s_in[:, heads])
+    ref = oracle.linear_attention_rows(qn, kn, vn, rows, sn)
+    got = f64(o[:, heads].cpu())[:, :, rows]
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    print(f"sampled rows: rel-fro {rel:.2e}")
+    assert np.isfinite(f64(o)).all()
+    assert rel <= 2.0 ** -7
+    rs = sn + np.einsum("bgjd,bgje->bgde", kn, vn)
+    srel = np.abs(f64(so[:, heads].cpu()) - rs).max() / np.abs(rs).max()
+    print(f"state: max-abs/max {srel:.2e}")
+    assert srel <= 1e-5

@@ -85,4 +85,5 @@ def test_gated_mlp_brute_force_reductions_and_shards():
 
 
 def test_linear_attention_brute_chunked_state_passing_and_closed_forms():
-    P.check_linear_attention(oracle.linear_attention, oracle.linear_attention_chunked, brute)
+    P.check_linear_attention(oracle.linear_attention, oracle.linear_attention_chunked, brute,
+                             oracle.linear_attention_rows)
