@@ -8,7 +8,7 @@ one JSON line: TFLOP/s (causal FLOPs = 4*B*Hq*S*S*D/2), the roofline of the
 attention kernel, the float64 oracle timed on a bounded sample on the host,
 and secondary figures for the other workloads (4096-token MHA forward and
 backward, the ring share with its log-sum-exp merge, the MLP chain plain and
-gated).
+gated, one share of linear attention with a carried state).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
        [--no-cpu-baseline]
@@ -121,9 +121,10 @@ def cpu_baseline(w, inputs, budget_s=12.0):
 
 def secondary(torch, chain, steps):
     """Other workloads: MHA 4096 forward and backward, ring share + merge, MLP chain
-    (plain and gated)."""
+    (plain and gated), linear attention share."""
     import numpy as np
-    from gemm_chain_amd.workloads import WORKLOADS, gen_attention, gen_attention_grad, gen_mlp, gen_mlp_gated
+    from gemm_chain_amd.workloads import (WORKLOADS, gen_attention, gen_attention_grad, gen_linear_state,
+                                          gen_mlp, gen_mlp_gated)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     out = {}
@@ -218,6 +219,24 @@ def secondary(torch, chain, steps):
                      steps, 2, stream)
     out[w.name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                    "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    del x, wg, wu, wd, o, ws
+
+    # One device's share of causal linear attention with a carried state (LASP):
+    # HBM-bound; algorithmic bytes = Q, K, V read, O (f32) written, states in and out.
+    w = WORKLOADS["lin_attn_bf16_h32_s32768_d128"]
+    q, k, v = (t.to(dev) for t in gen_attention(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.amp, w.seed))
+    s_in = gen_linear_state(w.B, w.Hkv, w.D, 1.0, w.seed + 1).to(dev)
+    o = torch.empty((w.B, w.Hq, w.S, w.D), dtype=torch.float32, device=dev)
+    s_out = torch.empty_like(s_in)
+    ws = torch.empty(chain.linear_attn_workspace_bytes(w.B, w.Hkv, w.S, w.D), dtype=torch.uint8, device=dev)
+    ms = time_region(torch, lambda: chain.linear_attn_fwd(q, k, v, s_in=s_in, out=o, s_out=s_out, workspace=ws),
+                     steps, 2, stream)
+    T = (w.S + 127) // 128
+    flops = w.B * w.Hq * (T * 4 * w.D * 128 * 129 / 2 + 2 * w.S * w.D * w.D) + w.B * w.Hkv * 2 * w.S * w.D * w.D
+    alg = 3 * q.numel() * 2 + o.numel() * 4 + 2 * s_in.numel() * 4
+    out[w.name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                   "gbs_algorithmic": round(alg / ms / 1e6, 1),
+                   "frac_hbm": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4)}
     return out
 
 
