@@ -581,8 +581,13 @@ chain_status chain_linear_attn_fwd(const chain_tensor *Q, const chain_tensor *K,
   p.q = Q->data, p.k = K->data, p.v = V->data, p.o = O->data;
   p.s_in = S_in ? (const float *)S_in->data : nullptr;
   p.s_out = S_out ? (float *)S_out->data : nullptr;
-  p.delta = (float *)workspace;
-  p.pref = workspace ? (__bf16 *)((char *)workspace + chain::linear_attn_pref_offset(B, Hkv, S, D)) : nullptr;
+  if (workspace) {
+    size_t off[4];
+    chain::linear_attn_workspace_layout(B, Hkv, S, D, off);
+    p.pref = (__bf16 *)((char *)workspace + off[0]);
+    p.seg_total = (float *)((char *)workspace + off[1]);
+    p.seg_base = (__bf16 *)((char *)workspace + off[2]);
+  }
   p.q_sb = Q->stride[0], p.q_sh = Q->stride[1], p.q_ss = Q->stride[2];
   p.k_sb = K->stride[0], p.k_sh = K->stride[1], p.k_ss = K->stride[2];
   p.v_sb = V->stride[0], p.v_sh = V->stride[1], p.v_ss = V->stride[2];

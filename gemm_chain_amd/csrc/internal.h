@@ -195,8 +195,9 @@ struct LinAttnParams {
   void *o;                            // [B, Hq, S, D], f32 or bf16
   const float *s_in;                  // [B, Hkv, D_k, D_v] or null (zero state)
   float *s_out;                       // [B, Hkv, D_k, D_v] or null
-  float *delta;                       // workspace: per chunk K_t^T V_t, transposed, f32
-  __bf16 *pref;                       // workspace: state before each chunk, transposed, bf16
+  __bf16 *pref;                       // workspace: per chunk, the state since its segment start (bf16, transposed)
+  float *seg_total;                   // workspace: per segment, the sum of its chunks' K^T V (f32, transposed)
+  __bf16 *seg_base;                   // workspace: per segment, the state at its start (bf16, transposed)
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
@@ -215,6 +216,6 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnBwdParams &p, int D, hipStream_t stream);
 hipError_t launch_linear_attn(const LinAttnParams &p, int D, hipStream_t stream);
 size_t linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D);
-size_t linear_attn_pref_offset(int64_t B, int64_t Hkv, int64_t S, int64_t D);
+void linear_attn_workspace_layout(int64_t B, int64_t Hkv, int64_t S, int64_t D, size_t off[4]);
 
 }  // namespace chain

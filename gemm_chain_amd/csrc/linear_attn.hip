@@ -10,15 +10,17 @@
 // Evaluated over chunks of C = 128 rows (right product across chunks, left
 // product inside one):
 //   O_t = mask(Q_t K_t^T) V_t + Q_t S_{t-1},   S_t = S_{t-1} + K_t^T V_t,
-// in three kernels:
-//  - delta: per (b, g, chunk) the chunk's K_t^T V_t, stored transposed (row d_v,
-//    column d_k) in f32 in the workspace; both operands are read from LDS with
-//    ds_read_b64_tr_b16 (the contraction runs over the chunk's rows);
-//  - scan: per (b, g) the running state in f32, stored before each chunk is added
-//    as the bf16 operand of the output kernel (the state cache), and S_out;
+// in three kernels, with the state scanned on two levels (segments of 16
+// chunks), so that no per-chunk f32 state ever goes to memory:
+//  - seg: per (b, g, segment) the chunks' K_t^T V_t accumulate in MFMA
+//    registers (operands from LDS by ds_read_b64_tr_b16: the contraction runs
+//    over the chunk's rows); before each chunk the state since the segment start
+//    is stored in bf16 (the state cache), and the segment total in f32;
+//  - segscan: per (b, g) the state at each segment start (S_in plus earlier
+//    totals, f32, stored in bf16) and S_out;
 //  - out: per (b, h, chunk), four waves of 32 query rows: S^T = K.Q^T for the
 //    visible 32-key blocks (diagonal block masked), O^T += V^T.P^T with P the
-//    bf16 scores, then O^T += S_{t-1}^T.Q^T for all earlier rows at once.
+//    bf16 scores, then O^T += (base + prefix)^T.Q^T for all earlier rows.
 #include "internal.h"
 
 namespace chain {
@@ -33,6 +35,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 128;   // rows per chunk
+constexpr int kSeg = 16;      // chunks per segment of the two-level state scan
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -91,47 +94,88 @@ __device__ inline bf16x8 row_frag(const char *t, int r0, int ks, int lane) {
   return *(const bf16x8 *)(t + tile_off<D>(r0 + (lane & 31), 16 * ks + 8 * (lane >> 5)));
 }
 
-// ---- delta: K_t^T V_t of one chunk, stored transposed --------------------------
+// ---- seg: the state inside a segment of kSeg chunks, kept in MFMA accumulators
+// One workgroup per (b, g, segment).  Wave w owns rows 32w.. of S^T (D = 128;
+// D = 64: one 32 x 32 block per wave).  Before each chunk is added, the running
+// state since the segment start is stored in bf16 (the state cache); after the
+// last chunk the segment's total goes out in f32.  The next chunk's K and V are
+// loaded into registers while the current one is multiplied.
 template <int D>
-__global__ __launch_bounds__(256) void lin_delta_kernel(const LinAttnParams p) {
-  constexpr int DB = D / 32;
+__global__ __launch_bounds__(256) void lin_seg_kernel(const LinAttnParams p) {
+  constexpr int DB = D / 32, CPR = D / 8, NL = kChunk * CPR / 256;
   __shared__ __attribute__((aligned(16))) char lds[2 * kChunk * 2 * D];
   char *ks_ = lds, *vs_ = lds + kChunk * 2 * D;
-  const int T = (p.S + kChunk - 1) / kChunk;
-  const int t = blockIdx.x % T, bg = blockIdx.x / T;
+  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
+  const int s = blockIdx.x % NS, bg = blockIdx.x / NS;
   const int g = bg % p.Hkv, b = bg / p.Hkv;
-  const int r0 = t * kChunk, nrows = min(kChunk, p.S - r0);
-  stage_rows<D, kChunk>(ks_, (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh + r0 * p.k_ss, p.k_ss, nrows);
-  stage_rows<D, kChunk>(vs_, (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh + r0 * p.v_ss, p.v_ss, nrows);
-  __syncthreads();
+  const int t0 = s * kSeg, nt = min(kSeg, T - t0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h2 = lane >> 5, l32 = lane & 31;
-  // wave -> (d_v block, first d_k block); D = 128: one d_v block and all four d_k
-  // blocks per wave, D = 64: one (d_v, d_k) block pair per wave
   constexpr int NJ = D == 128 ? DB : 1;
   const int iv = D == 128 ? wave : wave >> 1;
   const int j0 = D == 128 ? 0 : wave & 1;
+  const __bf16 *kbase = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
+  const __bf16 *vbase = (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh;
+  u32x4 kr[NL], vr[NL];
+  auto load = [&](int t) {
+    const int r0 = t * kChunk, nrows = min(kChunk, p.S - r0);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int c = threadIdx.x + 256 * i, row = c / CPR, ch = c % CPR;
+      const bool ok = row < nrows;
+      kr[i] = ok ? *(const u32x4 *)(kbase + (int64_t)(r0 + row) * p.k_ss + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+      vr[i] = ok ? *(const u32x4 *)(vbase + (int64_t)(r0 + row) * p.v_ss + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int c = threadIdx.x + 256 * i, row = c / CPR, ch = c % CPR;
+      const int off = row * 2 * D + ((ch ^ swz<D>(row)) << 4);
+      *(u32x4 *)(ks_ + off) = kr[i];
+      *(u32x4 *)(vs_ + off) = vr[i];
+    }
+  };
   f32x16 acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
+  load(t0);
+  store();
+  __syncthreads();
+  for (int c = 0; c < nt; ++c) {
+    const int t = t0 + c;
+    if (c + 1 < nt) load(t + 1);
+    // the state since the segment start, before chunk t: acc[j][r] is S^T at
+    // d_v = 32 iv + 8(r/4) + 4h2 + r%4, d_k = 32 (j0 + j) + l32
+    __bf16 *pf = p.pref + ((int64_t)bg * T + t) * D * D;
 #pragma unroll
-  for (int ks = 0; ks < kChunk / 16; ++ks) {
-    const bf16x8 a = tr_frag<D>(vs_, 16 * ks, 32 * iv, lane);
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = mfma32(a, tr_frag<D>(ks_, 16 * ks, 32 * (j0 + j), lane), acc[j]);
+      for (int r = 0; r < 16; ++r)
+        pf[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32] = (__bf16)acc[j][r];
+#pragma unroll
+    for (int ks = 0; ks < kChunk / 16; ++ks) {
+      const bf16x8 a = tr_frag<D>(vs_, 16 * ks, 32 * iv, lane);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = mfma32(a, tr_frag<D>(ks_, 16 * ks, 32 * (j0 + j), lane), acc[j]);
+    }
+    if (c + 1 < nt) {
+      __syncthreads();
+      store();
+      __syncthreads();
+    }
   }
-  // acc[j][r]: d_v = 32 iv + 8(r/4) + 4h2 + r%4, d_k = 32 (j0 + j) + l32
-  float *dst = p.delta + ((int64_t)bg * T + t) * D * D;
+  float *tot = p.seg_total + ((int64_t)bg * NS + s) * D * D;
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      dst[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32] = acc[j][r];
+      tot[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32] = acc[j][r];
 }
 
-// ---- scan: the state before each chunk (bf16 cache) and S_out -----------------
+// ---- segscan: the state at each segment start (bf16) and S_out ------------------
 template <int D>
-__global__ __launch_bounds__(256) void lin_scan_kernel(const LinAttnParams p) {
-  const int T = (p.S + kChunk - 1) / kChunk;
+__global__ __launch_bounds__(256) void lin_segscan_kernel(const LinAttnParams p) {
+  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
   constexpr int PER_HEAD = D * D / 4 / 256;   // workgroups per head
   const int bg = blockIdx.x / PER_HEAD;
   const int e = ((blockIdx.x % PER_HEAD) * 256 + threadIdx.x) * 4;   // first of 4 elements
@@ -143,12 +187,10 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(const LinAttnParams p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) run[u] = si[(dk + u) * p.si_sr + dv];
   }
-  const float *dl = p.delta + (int64_t)bg * T * D * D + e;
-  __bf16 *pf = p.pref + (int64_t)bg * T * D * D + e;
-  for (int t = 0; t < T; ++t) {
-    const f32x4 d = *(const f32x4 *)(dl + (int64_t)t * D * D);
-    *(bf16x4 *)(pf + (int64_t)t * D * D) = bf16x4{(__bf16)run[0], (__bf16)run[1], (__bf16)run[2], (__bf16)run[3]};
-    run += d;
+  for (int s = 0; s < NS; ++s) {
+    const int64_t o = ((int64_t)bg * NS + s) * D * D + e;
+    *(bf16x4 *)(p.seg_base + o) = bf16x4{(__bf16)run[0], (__bf16)run[1], (__bf16)run[2], (__bf16)run[3]};
+    run += *(const f32x4 *)(p.seg_total + o);
   }
   if (p.s_out) {
     float *so = p.s_out + b * p.so_sb + g * p.so_sh;
@@ -161,9 +203,9 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(const LinAttnParams p) {
 template <int D>
 __global__ __launch_bounds__(256) void lin_out_kernel(const LinAttnParams p) {
   constexpr int KS = D / 16, DB = D / 32, RB = 2 * D;
-  __shared__ __attribute__((aligned(16))) char lds[(2 * kChunk + D) * RB];
-  char *ks_ = lds, *vs_ = lds + kChunk * RB, *ss_ = lds + 2 * kChunk * RB;
-  const int T = (p.S + kChunk - 1) / kChunk;
+  __shared__ __attribute__((aligned(16))) char lds[(2 * kChunk + 2 * D) * RB];
+  char *ks_ = lds, *vs_ = lds + kChunk * RB, *ss_ = lds + 2 * kChunk * RB, *sb_ = ss_ + D * RB;
+  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
   const int t = blockIdx.x % T, bh = blockIdx.x / T;
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int g = h / (p.Hq / p.Hkv);
@@ -171,6 +213,7 @@ __global__ __launch_bounds__(256) void lin_out_kernel(const LinAttnParams p) {
   stage_rows<D, kChunk>(ks_, (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh + r0 * p.k_ss, p.k_ss, nrows);
   stage_rows<D, kChunk>(vs_, (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh + r0 * p.v_ss, p.v_ss, nrows);
   stage_rows<D, D>(ss_, p.pref + ((int64_t)(b * p.Hkv + g) * T + t) * D * D, D, D);
+  stage_rows<D, D>(sb_, p.seg_base + ((int64_t)(b * p.Hkv + g) * NS + t / kSeg) * D * D, D, D);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h2 = lane >> 5, l32 = lane & 31;
   const int row = 32 * wave + l32;   // query row within the chunk
   const bool row_ok = row < nrows;
@@ -202,11 +245,15 @@ __global__ __launch_bounds__(256) void lin_out_kernel(const LinAttnParams p) {
       for (int hh = 0; hh < 2; ++hh)
         acc[db] = mfma32(tr_frag<D>(vs_, 32 * kb + 16 * hh, 32 * db, lane), pk[hh], acc[db]);
   }
-  // earlier chunks through the carried state: O^T += S^T . Q^T
+  // earlier chunks through the carried state, the segment's base and the prefix
+  // inside the segment: O^T += S^T . Q^T
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc[db] = mfma32(row_frag<D>(ss_, 32 * db, ks, lane), qf[ks], acc[db]);
+    for (int ks = 0; ks < KS; ++ks) {
+      acc[db] = mfma32(row_frag<D>(sb_, 32 * db, ks, lane), qf[ks], acc[db]);
+      acc[db] = mfma32(row_frag<D>(ss_, 32 * db, ks, lane), qf[ks], acc[db]);
+    }
   if (row_ok) {
     const int64_t orow = b * p.o_sb + h * p.o_sh + (int64_t)(r0 + row) * p.o_ss;
 #pragma unroll
@@ -223,33 +270,39 @@ __global__ __launch_bounds__(256) void lin_out_kernel(const LinAttnParams p) {
 
 template <int D>
 hipError_t launch_d(const LinAttnParams &p, hipStream_t s) {
-  const int T = (p.S + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(lin_delta_kernel<D>, dim3(p.B * p.Hkv * T), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(lin_scan_kernel<D>, dim3(p.B * p.Hkv * (D * D / 1024)), dim3(256), 0, s, p);
+  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
+  hipLaunchKernelGGL(lin_seg_kernel<D>, dim3(p.B * p.Hkv * NS), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(lin_segscan_kernel<D>, dim3(p.B * p.Hkv * (D * D / 1024)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(lin_out_kernel<D>, dim3(p.B * p.Hq * T), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D) {
-  const int64_t T = (S + kChunk - 1) / kChunk;
-  const size_t per = (size_t)B * Hkv * T * D * D;
-  return (per * 4 + 255) / 256 * 256 + (per * 2 + 255) / 256 * 256;
+// Workspace: [in-segment prefix per chunk, bf16 | segment totals, f32 | segment bases, bf16].
+void linear_attn_workspace_layout(int64_t B, int64_t Hkv, int64_t S, int64_t D, size_t off[4]) {
+  const int64_t T = (S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
+  const size_t per_chunk = (size_t)B * Hkv * T * D * D, per_seg = (size_t)B * Hkv * NS * D * D;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  off[0] = 0;
+  off[1] = off[0] + up(per_chunk * 2);
+  off[2] = off[1] + up(per_seg * 4);
+  off[3] = off[2] + up(per_seg * 2);
 }
 
-size_t linear_attn_pref_offset(int64_t B, int64_t Hkv, int64_t S, int64_t D) {
-  const int64_t T = (S + kChunk - 1) / kChunk;
-  return ((size_t)B * Hkv * T * D * D * 4 + 255) / 256 * 256;
+size_t linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D) {
+  size_t off[4];
+  linear_attn_workspace_layout(B, Hkv, S, D, off);
+  return off[3];
 }
 
 hipError_t launch_linear_attn(const LinAttnParams &p, int D, hipStream_t s) {
   if (p.B == 0 || p.Hkv == 0) return hipSuccess;
   if (p.S == 0) {
-    // no rows: S_out = S_in (or 0); the scan with zero chunks writes exactly that
+    // no rows: S_out = S_in (or 0); the scan over zero segments writes exactly that
     if (!p.s_out) return hipSuccess;
-    if (D == 64) hipLaunchKernelGGL(lin_scan_kernel<64>, dim3(p.B * p.Hkv * 4), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(lin_scan_kernel<128>, dim3(p.B * p.Hkv * 16), dim3(256), 0, s, p);
+    if (D == 64) hipLaunchKernelGGL(lin_segscan_kernel<64>, dim3(p.B * p.Hkv * 4), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(lin_segscan_kernel<128>, dim3(p.B * p.Hkv * 16), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   return D == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);

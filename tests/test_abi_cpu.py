@@ -347,7 +347,8 @@ def test_linear_attn_validation_codes(lib):
     Si = td([1, 2, 128, 128], chain.F32, FAKE + 4 * G)
     So = td([1, 2, 128, 128], chain.F32, FAKE + 5 * G)
     need = lib.chain_linear_attn_workspace_bytes(1, 2, 256, 128)
-    assert need == 2 * 2 * 128 * 128 * 6     # two chunks: f32 deltas + bf16 states
+    # two chunks of bf16 in-segment states, one segment's f32 total and bf16 base
+    assert need == 2 * 2 * 128 * 128 * 2 + 2 * 128 * 128 * 6
     ws = FAKE + 6 * G
 
     def call(q=Q, k=K, v=V, o=O, si=Si, so=So, w=ws, n=need):
