@@ -286,11 +286,11 @@ size_t chain_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t S);
  *   S_in   [B, Hkv, D, D]   f32 (input; NULL = zero state, the first share)
  *   S_out  [B, Hkv, D, D]   f32 (output; NULL to skip)
  *   workspace  at least chain_linear_attn_workspace_bytes(B, Hkv, S, D) bytes,
- *              256-byte aligned; caller-owned scratch holding, per 128-row chunk,
- *              K_t^T V_t (f32) and the state before the chunk (bf16, the second
- *              product's MFMA operand)
- * Products are bf16 MFMAs with f32 accumulation; the in-chunk scores are rounded
- * to bf16 as an MFMA operand.  D must be 64 or 128.  The last dimension of every
+ *              256-byte aligned; caller-owned scratch (the cached states: per
+ *              128-row chunk the state since its 16-chunk segment began, per
+ *              segment its total and the state at its start)
+ * Products are bf16 MFMAs with f32 accumulation; the in-chunk scores and the two
+ * parts of each chunk's carried state are rounded to bf16 as MFMA operands.  D must be 64 or 128.  The last dimension of every
  * tensor is contiguous; Q, K, V, O 16-byte aligned, the states 4-byte aligned.
  * S == 0 is valid (S_out = S_in).  Outputs and workspace must not overlap inputs
  * or each other.
