@@ -582,11 +582,10 @@ chain_status chain_linear_attn_fwd(const chain_tensor *Q, const chain_tensor *K,
   p.s_in = S_in ? (const float *)S_in->data : nullptr;
   p.s_out = S_out ? (float *)S_out->data : nullptr;
   if (workspace) {
-    size_t off[4];
+    size_t off[3];
     chain::linear_attn_workspace_layout(B, Hkv, S, D, off);
-    p.pref = (__bf16 *)((char *)workspace + off[0]);
-    p.seg_total = (float *)((char *)workspace + off[1]);
-    p.seg_base = (__bf16 *)((char *)workspace + off[2]);
+    p.sub_total = (float *)((char *)workspace + off[0]);
+    p.seg_base = (float *)((char *)workspace + off[1]);
   }
   p.q_sb = Q->stride[0], p.q_sh = Q->stride[1], p.q_ss = Q->stride[2];
   p.k_sb = K->stride[0], p.k_sh = K->stride[1], p.k_ss = K->stride[2];

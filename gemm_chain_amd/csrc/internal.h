@@ -195,9 +195,8 @@ struct LinAttnParams {
   void *o;                            // [B, Hq, S, D], f32 or bf16
   const float *s_in;                  // [B, Hkv, D_k, D_v] or null (zero state)
   float *s_out;                       // [B, Hkv, D_k, D_v] or null
-  __bf16 *pref;                       // workspace: per chunk, the state since its segment start (bf16, transposed)
-  float *seg_total;                   // workspace: per segment, the sum of its chunks' K^T V (f32, transposed)
-  __bf16 *seg_base;                   // workspace: per segment, the state at its start (bf16, transposed)
+  float *sub_total;                   // workspace: per sub-segment, the sum of its chunks' K^T V (f32, [D_k, D_v])
+  float *seg_base;                    // workspace: per segment, the state at its start (f32, [D_k, D_v])
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
@@ -206,6 +205,8 @@ struct LinAttnParams {
   int64_t so_sb, so_sh, so_sr;
   int32_t B, Hq, Hkv, S;
   int32_t o_f32;
+  int32_t sub_len, n_sub;             // chunks per sub-segment; sub-segments per head
+  int32_t seg_subs, n_seg;            // sub-segments per segment; segments per head
 };
 
 // Launchers (defined in the .hip files).  Each returns the launch's hipError_t.
@@ -216,6 +217,6 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnBwdParams &p, int D, hipStream_t stream);
 hipError_t launch_linear_attn(const LinAttnParams &p, int D, hipStream_t stream);
 size_t linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D);
-void linear_attn_workspace_layout(int64_t B, int64_t Hkv, int64_t S, int64_t D, size_t off[4]);
+void linear_attn_workspace_layout(int64_t B, int64_t Hkv, int64_t S, int64_t D, size_t off[3]);
 
 }  // namespace chain

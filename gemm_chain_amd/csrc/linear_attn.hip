@@ -10,18 +10,28 @@
 // Evaluated over chunks of C = 128 rows (right product across chunks, left
 // product inside one):
 //   O_t = mask(Q_t K_t^T) V_t + Q_t S_{t-1},   S_t = S_{t-1} + K_t^T V_t,
-// in three kernels, with the state scanned on two levels (segments of 16
-// chunks), so that no per-chunk f32 state ever goes to memory:
-//  - seg: per (b, g, segment) the chunks' K_t^T V_t accumulate in MFMA
-//    registers (operands from LDS by ds_read_b64_tr_b16: the contraction runs
-//    over the chunk's rows); before each chunk the state since the segment start
-//    is stored in bf16 (the state cache), and the segment total in f32;
-//  - segscan: per (b, g) the state at each segment start (S_in plus earlier
-//    totals, f32, stored in bf16) and S_out;
-//  - out: per (b, h, chunk), four waves of 32 query rows: S^T = K.Q^T for the
-//    visible 32-key blocks (diagonal block masked), O^T += V^T.P^T with P the
-//    bf16 scores, then O^T += (base + prefix)^T.Q^T for all earlier rows.
+// in two passes over the sequence with a short scan between them; no per-chunk
+// state ever goes to memory:
+//  - sub: per (b, g, sub-segment of consecutive chunks) the sum of the chunks'
+//    K_t^T V_t, accumulated in MFMA registers (both operands from LDS by
+//    ds_read_b64_tr_b16: the contraction runs over the chunk's rows), stored in f32;
+//  - scan: per (b, g) the state at the start of each segment (a run of
+//    consecutive sub-segments; S_in plus the earlier sums, f32) and S_out;
+//  - out: per (b, h, segment) one workgroup walks the segment's rows in order
+//    with the state in f32 MFMA registers, in pieces of 64 rows (D = 128, so
+//    that two workgroups fit per CU) or 128 rows (D = 64).  Per piece, each wave
+//    takes 32 query rows and a share of the d_v columns: S^T = K.Q^T for the
+//    visible 32-key blocks (the diagonal block masked), O^T += V^T.P^T with P
+//    the bf16 scores, and O^T += S^T.Q^T with the state before the piece rounded
+//    to bf16 once, through LDS; then the state takes the piece's K^T V.  The
+//    next piece's Q, K and V are loaded into registers while the current one is
+//    computed, and its O is stored after the next piece is staged.
+// Sub-segments are sized so that the first pass fills the chip; a segment is as
+// many sub-segments as the key/value head has query heads (at most), so that
+// the out pass has about as many workgroups again.
 #include "internal.h"
+
+#include <algorithm>
 
 namespace chain {
 namespace {
@@ -34,8 +44,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunk = 128;   // rows per chunk
-constexpr int kSeg = 16;      // chunks per segment of the two-level state scan
+constexpr int kChunk = 128;   // rows per chunk (the unit of the sub-segments)
+constexpr int kFill = 512;    // workgroups each pass aims at (two per compute unit)
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -62,18 +72,31 @@ __device__ inline int tile_off(int row, int col) {
   return row * 2 * D + ((((col >> 3) ^ swz<D>(row))) << 4) + 2 * (col & 7);
 }
 
-// Stage R rows of D bf16 (global row stride ld elements; rows >= nrows zero).
-template <int D, int R>
-__device__ inline void stage_rows(char *dst, const __bf16 *src, int64_t ld, int nrows) {
-  constexpr int CPR = D / 8, N = R * CPR / 256;
+// R rows of D bf16 in registers (16 bytes per thread and load), in the order a
+// staged tile is written; rows >= nrows are staged as zero.
+template <int D, int R = kChunk>
+struct ChunkRegs {
+  static constexpr int CPR = D / 8, NL = R * CPR / 256;
+  u32x4 r[NL];
+  int n;
+  // rows past the end read the last row (every load stays inside the tensor) and
+  // are written as zero
+  __device__ inline void load(const __bf16 *src, int64_t ld, int nrows) {
+    n = nrows;
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int c = threadIdx.x + 256 * i, row = c / CPR, ch = c % CPR;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < nrows) v = *(const u32x4 *)(src + row * ld + 8 * ch);
-    *(u32x4 *)(dst + row * 2 * D + ((ch ^ swz<D>(row)) << 4)) = v;
+    for (int i = 0; i < NL; ++i) {
+      const int c = threadIdx.x + 256 * i, row = c / CPR, ch = c % CPR;
+      r[i] = *(const u32x4 *)(src + min(row, nrows - 1) * ld + 8 * ch);
+    }
   }
-}
+  __device__ inline void store(char *dst) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int c = threadIdx.x + 256 * i, row = c / CPR, ch = c % CPR;
+      *(u32x4 *)(dst + row * 2 * D + ((ch ^ swz<D>(row)) << 4)) = row < n ? r[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+};
 
 // A-operand fragment of T^T for a staged row-major tile T: columns c0 + lane%32,
 // rows r0 + {4h..4h+3, 8+4h..8+4h+3} for lane half h (the same fragment serves as
@@ -94,77 +117,54 @@ __device__ inline bf16x8 row_frag(const char *t, int r0, int ks, int lane) {
   return *(const bf16x8 *)(t + tile_off<D>(r0 + (lane & 31), 16 * ks + 8 * (lane >> 5)));
 }
 
-// ---- seg: the state inside a segment of kSeg chunks, kept in MFMA accumulators
-// One workgroup per (b, g, segment).  Wave w owns rows 32w.. of S^T (D = 128;
-// D = 64: one 32 x 32 block per wave).  Before each chunk is added, the running
-// state since the segment start is stored in bf16 (the state cache); after the
-// last chunk the segment's total goes out in f32.  The next chunk's K and V are
-// loaded into registers while the current one is multiplied.
+// ---- sub: the sum of K_t^T V_t over one sub-segment's chunks ------------------
+// One workgroup per (b, g, sub-segment).  D = 128: wave w owns the d_k rows
+// 32w.. of S and all d_v columns; D = 64: one 32 x 32 block per wave.  The next
+// chunk's K and V are loaded into registers while the current one is multiplied.
 template <int D>
-__global__ __launch_bounds__(256) void lin_seg_kernel(const LinAttnParams p) {
-  constexpr int DB = D / 32, CPR = D / 8, NL = kChunk * CPR / 256;
+__global__ __launch_bounds__(256) void lin_sub_kernel(const LinAttnParams p) {
+  constexpr int NJ = D == 128 ? D / 32 : 1;
   __shared__ __attribute__((aligned(16))) char lds[2 * kChunk * 2 * D];
   char *ks_ = lds, *vs_ = lds + kChunk * 2 * D;
-  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
-  const int s = blockIdx.x % NS, bg = blockIdx.x / NS;
+  const int T = (p.S + kChunk - 1) / kChunk;
+  const int s = blockIdx.x % p.n_sub, bg = blockIdx.x / p.n_sub;
   const int g = bg % p.Hkv, b = bg / p.Hkv;
-  const int t0 = s * kSeg, nt = min(kSeg, T - t0);
+  const int t0 = s * p.sub_len, nt = min(p.sub_len, T - t0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h2 = lane >> 5, l32 = lane & 31;
-  constexpr int NJ = D == 128 ? DB : 1;
-  const int iv = D == 128 ? wave : wave >> 1;
-  const int j0 = D == 128 ? 0 : wave & 1;
+  const int iv = D == 128 ? wave : wave >> 1;   // d_k block
+  const int j0 = D == 128 ? 0 : wave & 1;       // first d_v block
   const __bf16 *kbase = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
   const __bf16 *vbase = (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh;
-  u32x4 kr[NL], vr[NL];
+  ChunkRegs<D> kr, vr;
   auto load = [&](int t) {
-    const int r0 = t * kChunk, nrows = min(kChunk, p.S - r0);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = threadIdx.x + 256 * i, row = c / CPR, ch = c % CPR;
-      const bool ok = row < nrows;
-      kr[i] = ok ? *(const u32x4 *)(kbase + (int64_t)(r0 + row) * p.k_ss + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
-      vr[i] = ok ? *(const u32x4 *)(vbase + (int64_t)(r0 + row) * p.v_ss + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = threadIdx.x + 256 * i, row = c / CPR, ch = c % CPR;
-      const int off = row * 2 * D + ((ch ^ swz<D>(row)) << 4);
-      *(u32x4 *)(ks_ + off) = kr[i];
-      *(u32x4 *)(vs_ + off) = vr[i];
-    }
+    const int r0 = t * kChunk, n = min(kChunk, p.S - r0);
+    kr.load(kbase + (int64_t)r0 * p.k_ss, p.k_ss, n);
+    vr.load(vbase + (int64_t)r0 * p.v_ss, p.v_ss, n);
   };
   f32x16 acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
   load(t0);
-  store();
+  kr.store(ks_);
+  vr.store(vs_);
   __syncthreads();
   for (int c = 0; c < nt; ++c) {
-    const int t = t0 + c;
-    if (c + 1 < nt) load(t + 1);
-    // the state since the segment start, before chunk t: acc[j][r] is S^T at
-    // d_v = 32 iv + 8(r/4) + 4h2 + r%4, d_k = 32 (j0 + j) + l32
-    __bf16 *pf = p.pref + ((int64_t)bg * T + t) * D * D;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pf[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32] = (__bf16)acc[j][r];
+    if (c + 1 < nt) load(t0 + c + 1);
 #pragma unroll
     for (int ks = 0; ks < kChunk / 16; ++ks) {
-      const bf16x8 a = tr_frag<D>(vs_, 16 * ks, 32 * iv, lane);
+      const bf16x8 a = tr_frag<D>(ks_, 16 * ks, 32 * iv, lane);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[j] = mfma32(a, tr_frag<D>(ks_, 16 * ks, 32 * (j0 + j), lane), acc[j]);
+      for (int j = 0; j < NJ; ++j) acc[j] = mfma32(a, tr_frag<D>(vs_, 16 * ks, 32 * (j0 + j), lane), acc[j]);
     }
     if (c + 1 < nt) {
       __syncthreads();
-      store();
+      kr.store(ks_);
+      vr.store(vs_);
       __syncthreads();
     }
   }
-  float *tot = p.seg_total + ((int64_t)bg * NS + s) * D * D;
+  // acc[j][r] is S at d_k = 32 iv + 8(r/4) + 4h2 + r%4, d_v = 32 (j0 + j) + l32
+  float *tot = p.sub_total + ((int64_t)bg * p.n_sub + s) * D * D;
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -172,139 +172,215 @@ __global__ __launch_bounds__(256) void lin_seg_kernel(const LinAttnParams p) {
       tot[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32] = acc[j][r];
 }
 
-// ---- segscan: the state at each segment start (bf16) and S_out ------------------
+// ---- scan: the state at each segment start (f32) and S_out --------------------
 template <int D>
-__global__ __launch_bounds__(256) void lin_segscan_kernel(const LinAttnParams p) {
-  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
+__global__ __launch_bounds__(256) void lin_scan_kernel(const LinAttnParams p) {
   constexpr int PER_HEAD = D * D / 4 / 256;   // workgroups per head
   const int bg = blockIdx.x / PER_HEAD;
   const int e = ((blockIdx.x % PER_HEAD) * 256 + threadIdx.x) * 4;   // first of 4 elements
-  const int dv = e / D, dk = e % D;
+  const int dk = e / D, dv = e % D;
   const int g = bg % p.Hkv, b = bg / p.Hkv;
   f32x4 run = {0.f, 0.f, 0.f, 0.f};
   if (p.s_in) {
-    const float *si = p.s_in + b * p.si_sb + g * p.si_sh;
+    const float *si = p.s_in + b * p.si_sb + g * p.si_sh + dk * p.si_sr + dv;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) run[u] = si[(dk + u) * p.si_sr + dv];
+    for (int u = 0; u < 4; ++u) run[u] = si[u];
   }
-  for (int s = 0; s < NS; ++s) {
-    const int64_t o = ((int64_t)bg * NS + s) * D * D + e;
-    *(bf16x4 *)(p.seg_base + o) = bf16x4{(__bf16)run[0], (__bf16)run[1], (__bf16)run[2], (__bf16)run[3]};
-    run += *(const f32x4 *)(p.seg_total + o);
+  const int64_t head = (int64_t)bg * p.n_sub * D * D + e;
+  for (int i = 0; i < p.n_seg; ++i) {
+    *(f32x4 *)(p.seg_base + head + (int64_t)i * D * D) = run;
+    const int j1 = min((i + 1) * p.seg_subs, p.n_sub);
+    for (int j = i * p.seg_subs; j < j1; ++j) run += *(const f32x4 *)(p.sub_total + head + (int64_t)j * D * D);
   }
   if (p.s_out) {
-    float *so = p.s_out + b * p.so_sb + g * p.so_sh;
+    float *so = p.s_out + b * p.so_sb + g * p.so_sh + dk * p.so_sr + dv;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) so[(dk + u) * p.so_sr + dv] = run[u];
+    for (int u = 0; u < 4; ++u) so[u] = run[u];
   }
 }
 
-// ---- out: O_t = mask(Q_t K_t^T) V_t + Q_t S_{t-1} ------------------------------
+// ---- out: O_t = mask(Q_t K_t^T) V_t + Q_t S_{t-1}, one segment per workgroup ---
+// The segment is walked in pieces of CR rows (CR = 64 at D = 128, so that two
+// workgroups fit per CU; 128 at D = 64).  Wave w takes the 32 query rows of block
+// w % (CR/32) and DBW = D/32 / (4 / (CR/32)) of the d_v blocks.
 template <int D>
-__global__ __launch_bounds__(256) void lin_out_kernel(const LinAttnParams p) {
-  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D;
-  __shared__ __attribute__((aligned(16))) char lds[(2 * kChunk + 2 * D) * RB];
-  char *ks_ = lds, *vs_ = lds + kChunk * RB, *ss_ = lds + 2 * kChunk * RB, *sb_ = ss_ + D * RB;
-  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
-  const int t = blockIdx.x % T, bh = blockIdx.x / T;
+constexpr int out_rows() { return D == 128 ? 64 : 128; }
+
+// O^T of 32 query rows (columns l32), d_v blocks db0.. of the accumulators, to memory.
+template <int D, int DBW>
+__device__ inline void store_o(const LinAttnParams &p, const f32x16 (&acc)[DBW], int db0, int64_t orow, int h2) {
+  if (p.o_f32) {
+#pragma unroll
+    for (int i = 0; i < DBW; ++i)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        *(f32x4 *)((float *)p.o + orow + 32 * (db0 + i) + 8 * gg + 4 * h2) =
+            f32x4{acc[i][4 * gg], acc[i][4 * gg + 1], acc[i][4 * gg + 2], acc[i][4 * gg + 3]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < DBW; ++i)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        *(bf16x4 *)((__bf16 *)p.o + orow + 32 * (db0 + i) + 8 * gg + 4 * h2) =
+            bf16x4{(__bf16)acc[i][4 * gg], (__bf16)acc[i][4 * gg + 1], (__bf16)acc[i][4 * gg + 2],
+                   (__bf16)acc[i][4 * gg + 3]};
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void lin_out_kernel(const LinAttnParams p) {
+  constexpr int CR = out_rows<D>(), NQB = CR / 32, DBW = D / 32 / (4 / NQB);
+  constexpr int KS = D / 16, RB = 2 * D, NJ = D == 128 ? D / 32 : 1;
+  __shared__ __attribute__((aligned(16))) char lds[(3 * CR + D) * RB];
+  char *ks_ = lds, *vs_ = lds + CR * RB, *qs_ = lds + 2 * CR * RB, *ss_ = lds + 3 * CR * RB;
+  const int sg = blockIdx.x % p.n_seg, bh = blockIdx.x / p.n_seg;
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int g = h / (p.Hq / p.Hkv);
-  const int r0 = t * kChunk, nrows = min(kChunk, p.S - r0);
-  stage_rows<D, kChunk>(ks_, (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh + r0 * p.k_ss, p.k_ss, nrows);
-  stage_rows<D, kChunk>(vs_, (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh + r0 * p.v_ss, p.v_ss, nrows);
-  stage_rows<D, D>(ss_, p.pref + ((int64_t)(b * p.Hkv + g) * T + t) * D * D, D, D);
-  stage_rows<D, D>(sb_, p.seg_base + ((int64_t)(b * p.Hkv + g) * NS + t / kSeg) * D * D, D, D);
+  const int seg_len = p.seg_subs * p.sub_len;   // in kChunk-row chunks
+  const int t0 = sg * seg_len;
+  const int row_begin = t0 * kChunk;
+  const int row_end = (int)std::min<int64_t>((int64_t)(t0 + seg_len) * kChunk, p.S);
+  const int np = (row_end - row_begin + CR - 1) / CR;   // pieces of CR rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h2 = lane >> 5, l32 = lane & 31;
-  const int row = 32 * wave + l32;   // query row within the chunk
-  const bool row_ok = row < nrows;
-  bf16x8 qf[KS];
+  const int qb = wave % NQB;                    // the wave's query block
+  const int db0 = (wave / NQB) * DBW;           // its first d_v block of O
+  const int iv = D == 128 ? wave : wave >> 1;   // its d_k block of the state
+  const int j0 = D == 128 ? 0 : wave & 1;       // its first d_v block of the state
+  const int row = 32 * qb + l32;                // query row within the piece
+  const __bf16 *qbase = (const __bf16 *)p.q + b * p.q_sb + h * p.q_sh;
+  const __bf16 *kbase = (const __bf16 *)p.k + b * p.k_sb + g * p.k_sh;
+  const __bf16 *vbase = (const __bf16 *)p.v + b * p.v_sb + g * p.v_sh;
+  ChunkRegs<D, CR> kr, vr, qr;
+  auto load = [&](int r0) {
+    const int n = min(CR, p.S - r0);
+    kr.load(kbase + (int64_t)r0 * p.k_ss, p.k_ss, n);
+    vr.load(vbase + (int64_t)r0 * p.v_ss, p.v_ss, n);
+    qr.load(qbase + (int64_t)r0 * p.q_ss, p.q_ss, n);
+  };
+  // the state: st[j][r] is S at d_k = 32 iv + 8(r/4) + 4h2 + r%4, d_v = 32 (j0 + j) + l32
+  f32x16 st[NJ];
   {
-    const __bf16 *qr = (const __bf16 *)p.q + b * p.q_sb + h * p.q_sh + (int64_t)(r0 + min(row, nrows - 1)) * p.q_ss + 8 * h2;
+    const float *base = p.seg_base + ((int64_t)(b * p.Hkv + g) * p.n_sub + sg) * D * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? *(const bf16x8 *)(qr + 16 * ks) : bf16x8{};
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        st[j][r] = base[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32];
   }
+  // stage the loaded piece and the state (S^T in bf16: row d_v, 4 consecutive d_k per write)
+  auto stage = [&]() {
+    kr.store(ks_);
+    vr.store(vs_);
+    qr.store(qs_);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *(bf16x4 *)(ss_ + tile_off<D>(32 * (j0 + j) + l32, 32 * iv + 8 * rq + 4 * h2)) =
+            bf16x4{(__bf16)st[j][4 * rq], (__bf16)st[j][4 * rq + 1], (__bf16)st[j][4 * rq + 2], (__bf16)st[j][4 * rq + 3]};
+  };
+  load(row_begin);
+  stage();
   __syncthreads();
-  f32x16 acc[DB];
+  for (int c = 0; c < np; ++c) {
+    const int r0 = row_begin + c * CR, nrows = min(CR, p.S - r0);
+    const bool more = c + 1 < np;
+    if (more) load(r0 + CR);
+    f32x16 acc[DBW];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  // inside the chunk: key blocks 0..wave (the wave's queries precede later keys)
-  for (int kb = 0; kb <= wave; ++kb) {
-    f32x16 s = f32x16{};
+    for (int i = 0; i < DBW; ++i) acc[i] = f32x16{};
+    // inside the piece: key blocks 0..qb (the wave's queries precede later keys)
+    for (int kb = 0; kb <= qb; ++kb) {
+      f32x16 s = f32x16{};
+#pragma unroll 2
+      for (int ks = 0; ks < KS; ++ks) s = mfma32(row_frag<D>(ks_, 32 * kb, ks, lane), row_frag<D>(qs_, 32 * qb, ks, lane), s);
+      // s[r]: key 32 kb + 8(r/4) + 4h2 + r%4 of query row; mask keys past the query
+      bf16x8 pk[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma32(row_frag<D>(ks_, 32 * kb, ks, lane), qf[ks], s);
-    // s[r]: key 32 kb + 8(r/4) + 4h2 + r%4 of query row; mask keys past the query
-    bf16x8 pk[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-      pk[r >> 3][r & 7] = (__bf16)(kb < wave || key <= row ? s[r] : 0.f);
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        acc[db] = mfma32(tr_frag<D>(vs_, 32 * kb + 16 * hh, 32 * db, lane), pk[hh], acc[db]);
-  }
-  // earlier chunks through the carried state, the segment's base and the prefix
-  // inside the segment: O^T += S^T . Q^T
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      acc[db] = mfma32(row_frag<D>(sb_, 32 * db, ks, lane), qf[ks], acc[db]);
-      acc[db] = mfma32(row_frag<D>(ss_, 32 * db, ks, lane), qf[ks], acc[db]);
-    }
-  if (row_ok) {
-    const int64_t orow = b * p.o_sb + h * p.o_sh + (int64_t)(r0 + row) * p.o_ss;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int d0 = 32 * db + 8 * gg + 4 * h2;
-        const f32x4 v = {acc[db][4 * gg], acc[db][4 * gg + 1], acc[db][4 * gg + 2], acc[db][4 * gg + 3]};
-        if (p.o_f32) *(f32x4 *)((float *)p.o + orow + d0) = v;
-        else *(bf16x4 *)((__bf16 *)p.o + orow + d0) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        pk[r >> 3][r & 7] = (__bf16)(kb < qb || key <= row ? s[r] : 0.f);
       }
+#pragma unroll
+      for (int i = 0; i < DBW; ++i)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          acc[i] = mfma32(tr_frag<D>(vs_, 32 * kb + 16 * hh, 32 * (db0 + i), lane), pk[hh], acc[i]);
+    }
+    // earlier rows through the state before this piece: O^T += S^T . Q^T
+#pragma unroll
+    for (int i = 0; i < DBW; ++i)
+#pragma unroll 2
+      for (int ks = 0; ks < KS; ++ks)
+        acc[i] = mfma32(row_frag<D>(ss_, 32 * (db0 + i), ks, lane), row_frag<D>(qs_, 32 * qb, ks, lane), acc[i]);
+    if (more) {
+      // the state after this piece, then the next piece into LDS
+#pragma unroll
+      for (int ks = 0; ks < CR / 16; ++ks) {
+        const bf16x8 a = tr_frag<D>(ks_, 16 * ks, 32 * iv, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) st[j] = mfma32(a, tr_frag<D>(vs_, 16 * ks, 32 * (j0 + j), lane), st[j]);
+      }
+      __syncthreads();
+      stage();
+      __syncthreads();
+    }
+    // the stores drain while the next piece is computed
+    if (row < nrows) store_o<D, DBW>(p, acc, db0, b * p.o_sb + h * p.o_sh + (int64_t)(r0 + row) * p.o_ss, h2);
   }
 }
 
+// Sub-segment length and count for B * Hkv heads of S rows.
+struct LinPlan {
+  int64_t T, sub_len, n_sub;
+};
+
+LinPlan lin_plan(int64_t B, int64_t Hkv, int64_t S, int64_t D) {
+  LinPlan pl;
+  pl.T = (S + kChunk - 1) / kChunk;
+  const int64_t want = std::max<int64_t>(1, kFill / std::max<int64_t>(1, B * Hkv));
+  pl.sub_len = std::max<int64_t>(1, (pl.T + want - 1) / want);
+  pl.n_sub = (pl.T + pl.sub_len - 1) / pl.sub_len;
+  return pl;
+}
+
 template <int D>
-hipError_t launch_d(const LinAttnParams &p, hipStream_t s) {
-  const int T = (p.S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
-  hipLaunchKernelGGL(lin_seg_kernel<D>, dim3(p.B * p.Hkv * NS), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(lin_segscan_kernel<D>, dim3(p.B * p.Hkv * (D * D / 1024)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(lin_out_kernel<D>, dim3(p.B * p.Hq * T), dim3(256), 0, s, p);
+hipError_t launch_d(LinAttnParams p, hipStream_t s) {
+  const LinPlan pl = lin_plan(p.B, p.Hkv, p.S, D);
+  p.sub_len = (int32_t)pl.sub_len;
+  p.n_sub = (int32_t)pl.n_sub;
+  p.seg_subs = std::max(1, std::min(p.Hq / p.Hkv, p.n_sub));
+  p.n_seg = (p.n_sub + p.seg_subs - 1) / p.seg_subs;
+  if (p.n_sub > 0) hipLaunchKernelGGL(lin_sub_kernel<D>, dim3(p.B * p.Hkv * p.n_sub), dim3(256), 0, s, p);
+  if (p.n_seg > 0 || p.s_out)
+    hipLaunchKernelGGL(lin_scan_kernel<D>, dim3(p.B * p.Hkv * (D * D / 1024)), dim3(256), 0, s, p);
+  if (p.n_seg > 0) hipLaunchKernelGGL(lin_out_kernel<D>, dim3(p.B * p.Hq * p.n_seg), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Workspace: [in-segment prefix per chunk, bf16 | segment totals, f32 | segment bases, bf16].
-void linear_attn_workspace_layout(int64_t B, int64_t Hkv, int64_t S, int64_t D, size_t off[4]) {
-  const int64_t T = (S + kChunk - 1) / kChunk, NS = (T + kSeg - 1) / kSeg;
-  const size_t per_chunk = (size_t)B * Hkv * T * D * D, per_seg = (size_t)B * Hkv * NS * D * D;
+// Workspace: [sub-segment sums, f32 | segment start states, f32], each
+// [B, Hkv, n_sub, D_k, D_v].
+void linear_attn_workspace_layout(int64_t B, int64_t Hkv, int64_t S, int64_t D, size_t off[3]) {
+  const LinPlan pl = lin_plan(B, Hkv, S, D);
+  const size_t per = (size_t)B * Hkv * pl.n_sub * D * D * 4;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   off[0] = 0;
-  off[1] = off[0] + up(per_chunk * 2);
-  off[2] = off[1] + up(per_seg * 4);
-  off[3] = off[2] + up(per_seg * 2);
+  off[1] = up(per);
+  off[2] = off[1] + up(per);
 }
 
 size_t linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D) {
-  size_t off[4];
+  size_t off[3];
   linear_attn_workspace_layout(B, Hkv, S, D, off);
-  return off[3];
+  return off[2];
 }
 
 hipError_t launch_linear_attn(const LinAttnParams &p, int D, hipStream_t s) {
-  if (p.B == 0 || p.Hkv == 0) return hipSuccess;
-  if (p.S == 0) {
-    // no rows: S_out = S_in (or 0); the scan over zero segments writes exactly that
-    if (!p.s_out) return hipSuccess;
-    if (D == 64) hipLaunchKernelGGL(lin_segscan_kernel<64>, dim3(p.B * p.Hkv * 4), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(lin_segscan_kernel<128>, dim3(p.B * p.Hkv * 16), dim3(256), 0, s, p);
-    return hipGetLastError();
-  }
+  // no rows and no state to pass: nothing to launch
+  if (p.B == 0 || p.Hkv == 0 || (p.S == 0 && !p.s_out)) return hipSuccess;
   return D == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);
 }
 

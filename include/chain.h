@@ -286,12 +286,14 @@ size_t chain_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t S);
  *   S_in   [B, Hkv, D, D]   f32 (input; NULL = zero state, the first share)
  *   S_out  [B, Hkv, D, D]   f32 (output; NULL to skip)
  *   workspace  at least chain_linear_attn_workspace_bytes(B, Hkv, S, D) bytes,
- *              256-byte aligned; caller-owned scratch (the cached states: per
- *              128-row chunk the state since its 16-chunk segment began, per
- *              segment its total and the state at its start)
- * Products are bf16 MFMAs with f32 accumulation; the in-chunk scores and the two
- * parts of each chunk's carried state are rounded to bf16 as MFMA operands.  D must be 64 or 128.  The last dimension of every
- * tensor is contiguous; Q, K, V, O 16-byte aligned, the states 4-byte aligned.
+ *              256-byte aligned; caller-owned scratch (the cached states, f32:
+ *              per run of consecutive 128-row chunks the sum of their K^T V,
+ *              and the state at the start of each run of such runs)
+ * Products are bf16 MFMAs with f32 accumulation; the scores inside a piece of
+ * rows (64 rows at D = 128, 128 at D = 64) and the f32 state before each piece
+ * are rounded to bf16 as MFMA operands.  D must be 64 or 128.  The last
+ * dimension of every tensor is contiguous; Q, K, V, O 16-byte aligned, the
+ * states 4-byte aligned.
  * S == 0 is valid (S_out = S_in).  Outputs and workspace must not overlap inputs
  * or each other.
  */

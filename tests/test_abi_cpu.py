@@ -347,8 +347,10 @@ def test_linear_attn_validation_codes(lib):
     Si = td([1, 2, 128, 128], chain.F32, FAKE + 4 * G)
     So = td([1, 2, 128, 128], chain.F32, FAKE + 5 * G)
     need = lib.chain_linear_attn_workspace_bytes(1, 2, 256, 128)
-    # two chunks of bf16 in-segment states, one segment's f32 total and bf16 base
-    assert need == 2 * 2 * 128 * 128 * 2 + 2 * 128 * 128 * 6
+    # two heads x two one-chunk sub-segments: an f32 sum and an f32 start state each
+    assert need == 2 * (2 * 2 * 128 * 128 * 4)
+    # many heads: one sub-segment per head
+    assert lib.chain_linear_attn_workspace_bytes(4, 128, 100000, 64) == 2 * (4 * 128 * 64 * 64 * 4)
     ws = FAKE + 6 * G
 
     def call(q=Q, k=K, v=V, o=O, si=Si, so=So, w=ws, n=need):

@@ -2,14 +2,14 @@
 key/value state) against the float64 oracle.
 
 Tolerance, element by element, from where the kernels round (Q, K, V and S_in
-are the same values on both sides): the in-chunk scores q_i . k_j are rounded
-to bf16 as an MFMA operand, and so are the two parts of the state before each
-128-row chunk (the state at the start of its 16-chunk segment, and the sum of
-the segment's earlier chunks); everything else accumulates in f32.  So
-|error of O_ie| is at most
-eps * (sum_{j in chunk, j<=i} |s_ij| |v_je| + sum_d |q_id| (|B_de| + |L_de|))
+are the same values on both sides).  The output pass takes the rows in pieces
+(64 rows at D = 128, 128 at D = 64).  Inside a piece the scores q_i . k_j are
+rounded to bf16 as an MFMA operand; the state before the piece is rounded to
+bf16 once, from its f32 value; everything else accumulates in f32.  So, with j
+running over the piece, |error of O_ie| is at most
+eps * (sum_{j<=i} |s_ij| |v_je| + sum_d |q_id| |S_de|)
 plus the f32 accumulation, bounded by 2^-14 times the same sums with the state's
-own terms spelled out (sum_d |q_id| sum_{j<chunk} |k_jd| |v_je|), with
+own terms spelled out (sum_d |q_id| sum_{j before the piece} |k_jd| |v_je|), with
 eps = 2^-8 (twice bf16's unit roundoff), and doubled for second-order terms.
 The relative Frobenius error is also held to 2^-7.
 """
@@ -27,8 +27,11 @@ pytestmark = pytest.mark.gpu
 
 EPS = 2.0 ** -8
 ACC = 2.0 ** -14
-CHUNK = 128
-SEGMENT = 16 * CHUNK   # rows per segment of the two-level state scan
+
+
+def piece_rows(D):
+    """Rows the output pass takes at a time (the state is rounded once per piece)."""
+    return 64 if D == 128 else 128
 
 
 def _bound(q, k, v, s_in):
@@ -37,24 +40,21 @@ def _bound(q, k, v, s_in):
     Hkv = k.shape[1]
     group = Hq // Hkv
     s0 = np.zeros((B, Hkv, D, D)) if s_in is None else s_in
+    piece = piece_rows(D)
     bound = np.zeros(q.shape)
     for b in range(B):
         for h in range(Hq):
             g = h // group
-            base = s0[b, g].copy()                 # state at the segment start
-            local = np.zeros((D, D))               # the segment's earlier chunks
-            astate = np.abs(s0[b, g]).copy()       # the state's terms in absolute value
-            for t0 in range(0, S, CHUNK):
-                t1 = min(t0 + CHUNK, S)
-                if t0 % SEGMENT == 0:
-                    base += local
-                    local[:] = 0.0
+            state = s0[b, g].copy()                # the state before the chunk
+            astate = np.abs(s0[b, g]).copy()       # its terms in absolute value
+            for t0 in range(0, S, piece):
+                t1 = min(t0 + piece, S)
                 qa, ka, va = np.abs(q[b, h, t0:t1]), k[b, g, t0:t1], v[b, g, t0:t1]
                 sc = np.abs(q[b, h, t0:t1] @ ka.T) * np.tril(np.ones((t1 - t0, t1 - t0)))
                 intra = sc @ np.abs(va)
-                inter = qa @ (np.abs(base) + np.abs(local))
+                inter = qa @ np.abs(state)
                 bound[b, h, t0:t1] = 2 * (EPS * (intra + inter) + ACC * (intra + qa @ astate))
-                local += ka.T @ va
+                state += ka.T @ va
                 astate += np.abs(ka).T @ np.abs(va)
     return bound
 
@@ -77,7 +77,9 @@ CASES = [
     (1, 4, 4, 300, 128, True),     # ragged last chunk
     (2, 8, 2, 256, 64, False),     # GQA 4:1, D 64, whole chunks
     (1, 3, 1, 700, 128, True),     # GQA 3:1, six chunks
-    (1, 2, 2, 4500, 64, True),     # three segments of 16 chunks, the last ragged
+    (1, 2, 2, 4500, 64, True),     # 36 chunks, the last ragged
+    (1, 64, 64, 700, 128, True),   # many heads: sums over two-chunk sub-segments, ragged
+    (4, 64, 32, 1000, 64, True),   # GQA 2:1: two-chunk sub-segments, four-chunk walks
     (1, 2, 2, 129, 64, True),      # one row past a chunk
     (1, 2, 1, 1, 128, True),       # a single token
 ]
