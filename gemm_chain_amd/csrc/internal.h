@@ -207,6 +207,7 @@ struct LinAttnParams {
   int32_t o_f32;
   int32_t sub_len, n_sub;             // chunks per sub-segment; sub-segments per head
   int32_t seg_subs, n_seg;            // sub-segments per segment; segments per head
+  int32_t sub_per_wg;                 // sub-segments per workgroup of the first pass
 };
 
 // Launchers (defined in the .hip files).  Each returns the launch's hipError_t.

@@ -46,6 +46,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 128;   // rows per chunk (the unit of the sub-segments)
 constexpr int kFill = 512;    // workgroups each pass aims at (two per compute unit)
+constexpr int kSubFill = 256; // workgroups of the first pass (one per compute unit)
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -117,19 +118,22 @@ __device__ inline bf16x8 row_frag(const char *t, int r0, int ks, int lane) {
   return *(const bf16x8 *)(t + tile_off<D>(r0 + (lane & 31), 16 * ks + 8 * (lane >> 5)));
 }
 
-// ---- sub: the sum of K_t^T V_t over one sub-segment's chunks ------------------
-// One workgroup per (b, g, sub-segment).  D = 128: wave w owns the d_k rows
-// 32w.. of S and all d_v columns; D = 64: one 32 x 32 block per wave.  The next
-// chunk's K and V are loaded into registers while the current one is multiplied.
+// ---- sub: the sum of K_t^T V_t over each sub-segment's chunks ---------------
+// One workgroup per (b, g, run of sub_per_wg consecutive sub-segments).  D = 128:
+// wave w owns the d_k rows 32w.. of S and all d_v columns; D = 64: one 32 x 32
+// block per wave.  The next chunk's K and V are loaded into registers while the
+// current one is multiplied; each sub-segment's sum goes out as it completes.
 template <int D>
 __global__ __launch_bounds__(256) void lin_sub_kernel(const LinAttnParams p) {
   constexpr int NJ = D == 128 ? D / 32 : 1;
   __shared__ __attribute__((aligned(16))) char lds[2 * kChunk * 2 * D];
   char *ks_ = lds, *vs_ = lds + kChunk * 2 * D;
   const int T = (p.S + kChunk - 1) / kChunk;
-  const int s = blockIdx.x % p.n_sub, bg = blockIdx.x / p.n_sub;
+  const int nwg = (p.n_sub + p.sub_per_wg - 1) / p.sub_per_wg;   // workgroups per head
+  const int w = blockIdx.x % nwg, bg = blockIdx.x / nwg;
   const int g = bg % p.Hkv, b = bg / p.Hkv;
-  const int t0 = s * p.sub_len, nt = min(p.sub_len, T - t0);
+  const int s0 = w * p.sub_per_wg;
+  const int t0 = s0 * p.sub_len, tend = min(min(s0 + p.sub_per_wg, p.n_sub) * p.sub_len, T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h2 = lane >> 5, l32 = lane & 31;
   const int iv = D == 128 ? wave : wave >> 1;   // d_k block
   const int j0 = D == 128 ? 0 : wave & 1;       // first d_v block
@@ -148,28 +152,33 @@ __global__ __launch_bounds__(256) void lin_sub_kernel(const LinAttnParams p) {
   kr.store(ks_);
   vr.store(vs_);
   __syncthreads();
-  for (int c = 0; c < nt; ++c) {
-    if (c + 1 < nt) load(t0 + c + 1);
+  for (int t = t0; t < tend; ++t) {
+    const bool more = t + 1 < tend;
+    if (more) load(t + 1);
 #pragma unroll
     for (int ks = 0; ks < kChunk / 16; ++ks) {
       const bf16x8 a = tr_frag<D>(ks_, 16 * ks, 32 * iv, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[j] = mfma32(a, tr_frag<D>(vs_, 16 * ks, 32 * (j0 + j), lane), acc[j]);
     }
-    if (c + 1 < nt) {
+    if ((t + 1) % p.sub_len == 0 || !more) {
+      // acc[j][r] is S at d_k = 32 iv + 8(r/4) + 4h2 + r%4, d_v = 32 (j0 + j) + l32
+      float *tot = p.sub_total + ((int64_t)bg * p.n_sub + t / p.sub_len) * D * D;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tot[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32] = acc[j][r];
+        acc[j] = f32x16{};
+      }
+    }
+    if (more) {
       __syncthreads();
       kr.store(ks_);
       vr.store(vs_);
       __syncthreads();
     }
   }
-  // acc[j][r] is S at d_k = 32 iv + 8(r/4) + 4h2 + r%4, d_v = 32 (j0 + j) + l32
-  float *tot = p.sub_total + ((int64_t)bg * p.n_sub + s) * D * D;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      tot[(32 * iv + 8 * (r >> 2) + 4 * h2 + (r & 3)) * D + 32 * (j0 + j) + l32] = acc[j][r];
 }
 
 // ---- scan: the state at each segment start (f32) and S_out --------------------
@@ -352,7 +361,12 @@ hipError_t launch_d(LinAttnParams p, hipStream_t s) {
   p.n_sub = (int32_t)pl.n_sub;
   p.seg_subs = std::max(1, std::min(p.Hq / p.Hkv, p.n_sub));
   p.n_seg = (p.n_sub + p.seg_subs - 1) / p.seg_subs;
-  if (p.n_sub > 0) hipLaunchKernelGGL(lin_sub_kernel<D>, dim3(p.B * p.Hkv * p.n_sub), dim3(256), 0, s, p);
+  // the first pass reads only K and V: one workgroup per CU does best, each
+  // taking consecutive sub-segments
+  const int64_t heads = (int64_t)p.B * p.Hkv;
+  p.sub_per_wg = (int32_t)std::max<int64_t>(1, heads * p.n_sub / kSubFill);
+  const int64_t sub_wgs = heads * ((p.n_sub + p.sub_per_wg - 1) / p.sub_per_wg);
+  if (p.n_sub > 0) hipLaunchKernelGGL(lin_sub_kernel<D>, dim3(sub_wgs), dim3(256), 0, s, p);
   if (p.n_seg > 0 || p.s_out)
     hipLaunchKernelGGL(lin_scan_kernel<D>, dim3(p.B * p.Hkv * (D * D / 1024)), dim3(256), 0, s, p);
   if (p.n_seg > 0) hipLaunchKernelGGL(lin_out_kernel<D>, dim3(p.B * p.Hq * p.n_seg), dim3(256), 0, s, p);
