@@ -251,7 +251,7 @@ def main():
                     help="also run a plain device copy of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the sharded "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the sharded "
               "design is described, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -2,7 +2,7 @@
 
 Usage: python -m gemm_chain_amd.build   (or call build()).  Every source in
 csrc/ is compiled to an object under _build/ in parallel, then linked into
-gemm_chain_amd/libchain.so.  Always recompiles: the call is the build check.
+gemm_chain_amd/libchain.so.  Always recompiles, also over an existing library.
 """
 
 import os
