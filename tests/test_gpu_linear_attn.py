@@ -158,3 +158,43 @@ def test_linear_attention_full_size_sampled_rows():
     srel = np.abs(f64(so[:, heads].cpu()) - rs).max() / np.abs(rs).max()
     print(f"state: max-abs/max {srel:.2e}")
     assert srel <= 1e-5
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_linear_attention_bf16_output_and_no_state_out(D):
+    """A bf16 O is the f32 O rounded (same accumulation); S_out may be skipped."""
+    dev = device()
+    q, k, v = (t.to(dev) for t in gen_attention(1, 4, 2, 700, 700, D, "bf16", 0.5, 41))
+    s_in = gen_linear_state(1, 2, D, 1.0, 42).to(dev)
+    announce(f"linear_attn bf16 output D{D}")
+    o32, so = chain.linear_attn_fwd(q, k, v, s_in=s_in)
+    o16, none = chain.linear_attn_fwd(q, k, v, s_in=s_in, want_state=False, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert none is None and so is not None
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_linear_attention_strided_views_match_contiguous():
+    """Q, K, V and O as [B, S, H, D] storage viewed as [B, H, S, D], and states
+    with a padded row stride, give the contiguous call's bits."""
+    dev = device()
+    B, Hq, Hkv, S, D = 2, 4, 2, 300, 128
+    q, k, v = (t.to(dev) for t in gen_attention(B, Hq, Hkv, S, S, D, "bf16", 0.5, 43))
+    s_in = gen_linear_state(B, Hkv, D, 1.0, 44).to(dev)
+    announce("linear_attn strided views")
+    ref_o, ref_s = chain.linear_attn_fwd(q, k, v, s_in=s_in)
+
+    def bshd(t):
+        return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+    si_pad = torch.zeros(B, Hkv, D, D + 4, device=dev)
+    si_pad[..., :D] = s_in
+    so_pad = torch.full((B, Hkv, D, D + 4), 7.0, device=dev)
+    o = torch.full((B, S, Hq, D), 9.0, device=dev).transpose(1, 2)
+    got_o, got_s = chain.linear_attn_fwd(bshd(q), bshd(k), bshd(v), s_in=si_pad[..., :D],
+                                         out=o, s_out=so_pad[..., :D])
+    torch.cuda.synchronize()
+    assert torch.equal(got_o, ref_o)
+    assert torch.equal(got_s, ref_s)
+    assert torch.all(so_pad[..., D:] == 7.0)
