@@ -52,8 +52,12 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Transposing LDS read: in each group of 16 lanes, lane i receives element i%4
-// of the 4-element rows addressed by lanes 4e + i/4, e = 0..3.
-__device__ inline i16x4 ds_read_tr(const __bf16 *p) {
+// of the 4-element rows addressed by lanes 4e + i/4, e = 0..3.  The restrict
+// qualifier gives the read alias-scope information once inlined; without it the
+// compiler cannot tell the read from the direct-to-LDS loads in flight and
+// waits for all of them (vmcnt(0)) before every P.V run.  Every tile a read
+// touches has landed and passed a barrier, so no such wait is needed.
+__device__ inline i16x4 ds_read_tr(const __bf16 *__restrict__ p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
