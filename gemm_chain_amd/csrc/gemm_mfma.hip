@@ -8,16 +8,20 @@
 // [N, K] weight, as linear layers store it); the MLP runs it twice (act = GeLU
 // into the workspace, then act = identity).
 //
-// bf16: one 256-thread workgroup per CU (one wave per SIMD) computes a
-// 256 x BN tile (BN = 256, 192 or 128, picked per launch so the tiles fill
-// whole rounds of the chip), 2 x 2 waves of 128 x BN/2, each a 4 x BN/64 grid
-// of v_mfma_f32_32x32x16_bf16 blocks whose f32 accumulators live in AGPRs.
+// bf16: one workgroup per CU computes a 256 x BN tile (BN = 256, 192 or 128,
+// picked per launch so the tiles fill whole rounds of the chip) on
+// v_mfma_f32_32x32x16_bf16 blocks with f32 accumulators: 4 x 2 waves of
+// 64 x BN/2 (two waves per SIMD) for k-contiguous weights, 2 x 2 waves of
+// 128 x BN/2 (one wave per SIMD, accumulators in AGPRs) otherwise.
 // Operands are swapped in the MFMA (it computes the transposed block) so a lane
 // ends up holding four consecutive output columns of one row: 8-byte stores.
 // Two ways of feeding LDS, by weight layout:
-//  - k-contiguous B (gemm_bf16_dtl_kernel_NBW): loads that write LDS directly
-//    fill a ring of four k-stages of 32, fetched three stages ahead, rows
-//    XOR-swizzled instead of padded;
+//  - k-contiguous B: loads that write LDS directly fill a ring of four
+//    k-stages of 32, fetched three stages ahead, rows XOR-swizzled instead of
+//    padded.  gemm_bf16_w8_kernel_NBW runs eight waves (two per SIMD) of
+//    64 x BN/2 with buffer loads; gemm_bf16_dtl_kernel_NBW, the same ring with
+//    four waves of 128 x BN/2, serves operands whose 256-row tiles span 2 GiB
+//    or more (beyond 32-bit buffer offsets);
 //  - n-contiguous B (gemm_bf16_kernel<NBW>): k-tiles of 64 staged through
 //    registers into two LDS buffers; A as [256][64 + 8], B as [64][BN' + 32]
 //    read with ds_read_b64_tr_b16.
@@ -504,6 +508,217 @@ CHAIN_DTL_KERNELS(silu, CHAIN_ACT_SILU)
 #undef CHAIN_DTL_KERNELS
 #undef CHAIN_DTL_KERNEL
 
+// Eight-wave variant of the k-contiguous path (two waves per SIMD): a 256 x BN
+// tile as 4 x 2 waves of 64 x BN/2, each a 2 x NBW grid of 32 x 32 blocks with
+// f32 accumulators in registers.  The ring, the stage depth, the swizzle and
+// the k order are those of gemm_bf16_dtl (so both give the same bits); the
+// loads are buffer loads that write LDS directly, addressed by a descriptor
+// over the tile's rows (32-bit offsets: the host picks this kernel only when
+// a tile's rows span less than 2^31 bytes), with the stage's k offset in the
+// scalar offset operand.  A second wave on each SIMD issues MFMAs while the
+// other waits on its fragment reads or the barrier.
+template <int NBW, int ACT>
+__device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
+  constexpr int BN = 64 * NBW, WTN = 32 * NBW;
+  constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
+  constexpr int LA = BM / 16 / 8;               // 1 KB loads of A per wave and stage
+  constexpr int LBH = (NLB + 7) / 8, LBL = NLB / 8;   // of B: waves below NLB % 8 take LBH
+  __shared__ __attribute__((aligned(1024))) char lds[DST * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool hi = LBH == LBL || wave < NLB % 8;   // this wave takes LBH loads of B
+
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  constexpr int GM = 4;
+  const int g = t / (GM * tiles_n), fm = g * GM;
+  const int gmn = min(GM, tiles_m - fm), loc = t - g * GM * tiles_n;
+  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * BN;
+
+  // Descriptors over the tile's rows of A and of B (k contiguous in both).
+  const int ra = min(p.M - m0, BM), rb = min(p.N - n0, BN);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const __bf16 *)p.a + (int64_t)m0 * p.lda), 0,
+      (int)(((int64_t)(ra - 1) * p.lda + p.K) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const __bf16 *)p.b + (int64_t)n0 * p.b_sn), 0,
+      (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000);
+  // Lane i of a load fetches row i >> 2 of its 16-row group, logical chunk lc.
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t aoff[LA], boff[LBH];
+#pragma unroll
+  for (int q = 0; q < LA; ++q)
+    aoff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
+#pragma unroll
+  for (int q = 0; q < LBH; ++q)
+    boff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc;
+  const int nk = (p.K + DBK - 1) / DBK;
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  // Stage kt into ring slot kt % DST; past the last stage, stage 0 again (valid
+  // data into a slot nobody reads, so every iteration has the same shape).
+  auto issue = [&](int kt) {
+    char *sb = lds + (kt & (DST - 1)) * STAGE;
+    const int k0 = kt < nk ? kt * DBK : 0;
+    if (k0 + DBK <= p.K) {
+#pragma unroll
+      for (int q = 0; q < LA; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(sb + (wave + 8 * q) * 1024), 16, aoff[q],
+                                                 2 * k0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < LBH; ++q)
+        if (q < LBL || hi)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
+                                                   boff[q], 2 * k0, 0, 0);
+    } else {
+      // K tail: a chunk past K fetches k = K - 8 of its row instead
+      const uint32_t kb = 2u * (uint32_t)min(k0 + 8 * lc, p.K - 8) - 16u * lc;
+#pragma unroll
+      for (int q = 0; q < LA; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(sb + (wave + 8 * q) * 1024), 16, aoff[q] + kb,
+                                                 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < LBH; ++q)
+        if (q < LBL || hi)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
+                                                   boff[q] + kb, 0, 0, 0);
+    }
+  };
+  // After stage kt (the K tail) has landed: zero the chunks past K.
+  auto zero_tail = [&](int kt) {
+    if (kt * DBK + 8 * lc >= p.K) {
+      char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < LA; ++q) *(u32x4 *)(sb + (wave + 8 * q) * 1024) = z;
+#pragma unroll
+      for (int q = 0; q < LBH; ++q)
+        if (q < LBL || hi) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+    }
+  };
+  // This wave's loads of stage s have landed (stages s+1 and s+2 may still be
+  // in flight); zero the K tail if stage s holds it.
+  auto wait_stage = [&](int s) {
+    if (hi) wait_vmcnt<2 * (LA + LBH)>();
+    else wait_vmcnt<2 * (LA + LBL)>();
+    if (s < nk && s * DBK + DBK > p.K) zero_tail(s);
+  };
+
+  struct Frags {
+    bf16x8 a[2], b[NBW];
+  };
+  const int sx = (l32 >> 2) & 3;
+  const int pc0 = (h2 ^ sx) * 16, pc1 = ((2 + h2) ^ sx) * 16;
+  const int rowa = (wm * 64 + l32) * 64, rowb = A_BYTES + (wn * WTN + l32) * 64;
+  auto frags = [&](int kt, int ks, Frags &f) {
+    const char *sb = lds + (kt & (DST - 1)) * STAGE + (ks ? pc1 : pc0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = *(const bf16x8 *)(sb + rowa + i * 2048);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) f.b[j] = *(const bf16x8 *)(sb + rowb + j * 2048);
+  };
+
+  f32x16 acc[2][NBW];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](const Frags &f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+
+  constexpr int NM = 2 * NBW;   // MFMAs per k-step
+  Frags f0, f1;
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < DST - 1; ++s) issue(s);
+    wait_stage(0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    frags(0, 0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_lgkmcnt0();
+      __builtin_amdgcn_sched_barrier(0);
+      // stage kt+3 reuses the slot of stage kt-1, whose reads all came before
+      // the previous barrier
+      issue(kt + DST - 1);
+      frags(kt, 1, f1);
+      mfmas(f0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // load to LDS
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      wait_stage(kt + 1);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      frags(kt + 1, 0, f0);   // past the last stage: an unused read of a ring slot
+      mfmas(f1);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
+  }
+
+  auto store4 = [&](int gm, int gn, const f32x4 &v) {
+    const int64_t off = (int64_t)gm * p.ldc + gn;
+    if (p.c_f32) {
+      float *c = (float *)p.c + off;
+      if (p.c_vec) *(f32x4 *)c = v;
+      else c[0] = v[0], c[1] = v[1], c[2] = v[2], c[3] = v[3];
+    } else {
+      __bf16 *c = (__bf16 *)p.c + off;
+      const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      if (p.c_vec) *(bf16x4 *)c = w;
+      else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int gm = m0 + wm * 64 + i * 32 + l32;
+    if (gm >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
+        if (gn >= p.N) continue;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
+        store4(gm, gn, v);
+      }
+  }
+}
+
+#define CHAIN_W8_KERNEL(NAME, NBW, ACT)                                                       \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
+  void NAME(const GemmParams p) { gemm_bf16_w8<NBW, ACT>(p); }
+#define CHAIN_W8_KERNELS(SUFFIX, ACT)                              \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_2_##SUFFIX, 2, ACT)          \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_3_##SUFFIX, 3, ACT)          \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_4_##SUFFIX, 4, ACT)
+CHAIN_W8_KERNELS(erf, CHAIN_ACT_GELU_ERF)
+CHAIN_W8_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
+CHAIN_W8_KERNELS(id, CHAIN_ACT_IDENTITY)
+CHAIN_W8_KERNELS(silu, CHAIN_ACT_SILU)
+#undef CHAIN_W8_KERNELS
+#undef CHAIN_W8_KERNEL
+
 // f32 inputs: 128 x 128 x 32 tiles on v_mfma_f32_32x32x2_f32 (A: lane holds
 // A[m][k0 + h2], B: lane holds B[k0 + h2][n]); exact f32 products, f32
 // accumulation.
@@ -613,6 +828,23 @@ void launch_dtl(const GemmParams &p, int nbw, hipStream_t stream) {
   hipLaunchKernelGGL(ks[nbw - 2][p.act], dim3(tiles), dim3(256), 0, stream, p);
 }
 
+void launch_w8(const GemmParams &p, int nbw, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * nbw - 1) / (64 * nbw));
+  typedef void (*Kern)(const GemmParams);
+  static const Kern ks[3][4] = {
+      {gemm_bf16_w8_kernel_2_erf, gemm_bf16_w8_kernel_2_tanh, gemm_bf16_w8_kernel_2_id, gemm_bf16_w8_kernel_2_silu},
+      {gemm_bf16_w8_kernel_3_erf, gemm_bf16_w8_kernel_3_tanh, gemm_bf16_w8_kernel_3_id, gemm_bf16_w8_kernel_3_silu},
+      {gemm_bf16_w8_kernel_4_erf, gemm_bf16_w8_kernel_4_tanh, gemm_bf16_w8_kernel_4_id, gemm_bf16_w8_kernel_4_silu}};
+  hipLaunchKernelGGL(ks[nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
+}
+
+// The eight-wave kernel addresses a tile's rows with 32-bit byte offsets.
+bool w8_fits(const GemmParams &p, int nbw) {
+  const int64_t span_a = ((int64_t)(BM - 1) * p.lda + p.K) * 2;
+  const int64_t span_b = ((int64_t)(64 * nbw - 1) * p.b_sn + p.K) * 2;
+  return span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
+}
+
 int compute_units() {
   static thread_local int dev_cached = -1, cus = 256;
   int dev = 0;
@@ -648,7 +880,8 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
   } else if (dtype == CHAIN_BF16) {
     const int nbw = gemm_bf16_block_cols(p.M, p.N, compute_units());
     if (p.b_sk == 1) {
-      launch_dtl(p, nbw, stream);
+      if (w8_fits(p, nbw)) launch_w8(p, nbw, stream);
+      else launch_dtl(p, nbw, stream);
     } else {
       launch_bf16_width(p, nbw, stream);
     }
