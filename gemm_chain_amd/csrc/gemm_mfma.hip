@@ -840,8 +840,8 @@ void launch_w8(const GemmParams &p, int nbw, hipStream_t stream) {
 
 // The eight-wave kernel addresses a tile's rows with 32-bit byte offsets.
 bool w8_fits(const GemmParams &p, int nbw) {
-  const int64_t span_a = ((int64_t)(BM - 1) * p.lda + p.K) * 2;
-  const int64_t span_b = ((int64_t)(64 * nbw - 1) * p.b_sn + p.K) * 2;
+  const int64_t span_a = ((int64_t)(min(p.M, BM) - 1) * p.lda + p.K) * 2;
+  const int64_t span_b = ((int64_t)(min(p.N, 64 * nbw) - 1) * p.b_sn + p.K) * 2;
   return span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
 }
 

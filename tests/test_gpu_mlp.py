@@ -103,6 +103,28 @@ def test_mlp_weight_layouts_agree_and_match_oracle(M, K, N, K2):
     assert err <= TOL_BF16
 
 
+def test_mlp_row_stride_beyond_32bit_tile_offsets():
+    """X rows 4.4 M elements apart: a 256-row tile of X spans more than 2^31 bytes, so
+    X.W1 runs on the four-wave kernel (64-bit addresses) while H.W2 runs on the
+    eight-wave kernel; both use the same k order, so the result equals the contiguous
+    call's bit for bit."""
+    dev = device()
+    M, K, N, K2, lda = 300, 128, 136, 96, 4_400_000
+    x, w1, w2 = gen_mlp(M, K, N, K2, dtype="bf16", amp_x=1.0, amp_w=0.05, seed=75)
+    xd, w1d, w2d = x.to(dev), _kmajor(w1.to(dev)), _kmajor(w2.to(dev))
+    announce(f"mlp X row stride {lda} (tile span beyond 2^31 bytes)")
+    store = torch.zeros((M - 1) * lda + K, dtype=torch.bfloat16, device=dev)
+    xs = store.as_strided((M, K), (lda, 1))
+    xs.copy_(xd)
+    o = chain.mlp_fwd(xs, w1d, w2d, act="gelu_erf")
+    dense = chain.mlp_fwd(xd, w1d, w2d, act="gelu_erf")
+    torch.cuda.synchronize()
+    assert torch.equal(o, dense)
+    ref = oracle.mlp(f64(x), f64(w1), f64(w2), "gelu_erf")
+    assert max_abs(f64(o), ref) <= TOL_BF16
+    del store, xs
+
+
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_mlp_output_row_stride_not_vector_aligned(out_dtype):
     """An output whose row stride is not a multiple of 4 elements (element stores)."""
