@@ -517,9 +517,11 @@ CHAIN_DTL_KERNELS(silu, CHAIN_ACT_SILU)
 // a tile's rows span less than 2^31 bytes), with the stage's k offset in the
 // scalar offset operand.  A second wave on each SIMD issues MFMAs while the
 // other waits on its fragment reads or the barrier.
-template <int NBW, int ACT>
+template <int NBW, bool GATED, int ACT>
 __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   constexpr int BN = 64 * NBW, WTN = 32 * NBW;
+  constexpr int OBN = GATED ? BN / 2 : BN;   // output columns per tile
+  static_assert(!GATED || NBW % 2 == 0, "gated tiles pair 32-row blocks");
   constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
   constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
   constexpr int LA = BM / 16 / 8;               // 1 KB loads of A per wave and stage
@@ -531,21 +533,32 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   const int wm = wave >> 1, wn = wave & 1;
   const bool hi = LBH == LBL || wave < NLB % 8;   // this wave takes LBH loads of B
 
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + OBN - 1) / OBN;
   const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   constexpr int GM = 4;
   const int g = t / (GM * tiles_n), fm = g * GM;
   const int gmn = min(GM, tiles_m - fm), loc = t - g * GM * tiles_n;
-  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * BN;
+  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * OBN;
 
-  // Descriptors over the tile's rows of A and of B (k contiguous in both).
-  const int ra = min(p.M - m0, BM), rb = min(p.N - n0, BN);
+  // Descriptors over the tile's rows of A and of B (k contiguous in both; gated:
+  // one over the gate rows and one over the up rows of the tile's columns).
+  const int ra = min(p.M - m0, BM), rb = min(p.N - n0, OBN);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const __bf16 *)p.a + (int64_t)m0 * p.lda), 0,
       (int)(((int64_t)(ra - 1) * p.lda + p.K) * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const __bf16 *)p.b + (int64_t)n0 * p.b_sn), 0,
       (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs2 = GATED ? __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const __bf16 *)p.b2 + (int64_t)n0 * p.b_sn), 0,
+      (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000) : brs;
+  // Staged B row r holds output column n0 + bcol(r) of B, or (gated) of B2 when
+  // bup(r): each wave's 32-row blocks alternate gate, up for the same 32 columns.
+  auto bcol = [](int r) {
+    if (!GATED) return r;
+    return (r / WTN) * (WTN / 2) + ((r % WTN) / 32 >> 1) * 32 + r % 32;
+  };
+  auto bup = [](int r) { return GATED && (((r % WTN) / 32) & 1); };
   // Lane i of a load fetches row i >> 2 of its 16-row group, logical chunk lc.
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);
   uint32_t aoff[LA], boff[LBH];
@@ -554,7 +567,7 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
     aoff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
 #pragma unroll
   for (int q = 0; q < LBH; ++q)
-    boff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc;
+    boff[q] = (uint32_t)min(bcol(16 * (wave + 8 * q) + (lane >> 2)), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc;
   const int nk = (p.K + DBK - 1) / DBK;
   typedef __attribute__((address_space(3))) void lds_void;
 
@@ -571,7 +584,8 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
         if (q < LBL || hi)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bup(16 * (wave + 8 * q)) ? brs2 : brs,
+                                                   (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
                                                    boff[q], 2 * k0, 0, 0);
     } else {
       // K tail: a chunk past K fetches k = K - 8 of its row instead
@@ -583,7 +597,8 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
         if (q < LBL || hi)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bup(16 * (wave + 8 * q)) ? brs2 : brs,
+                                                   (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
                                                    boff[q] + kb, 0, 0, 0);
     }
   };
@@ -691,27 +706,43 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   for (int i = 0; i < 2; ++i) {
     const int gm = m0 + wm * 64 + i * 32 + l32;
     if (gm >= p.M) continue;
+    if constexpr (GATED) {
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
+      for (int u = 0; u < NBW / 2; ++u)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
-        if (gn >= p.N) continue;
-        f32x4 v;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int gn = n0 + wn * (WTN / 2) + u * 32 + 8 * r4 + 4 * h2;
+          if (gn >= p.N) continue;
+          f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
-        store4(gm, gn, v);
-      }
+          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][2 * u][4 * r4 + e], ACT) * acc[i][2 * u + 1][4 * r4 + e];
+          store4(gm, gn, v);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
+          if (gn >= p.N) continue;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
+          store4(gm, gn, v);
+        }
+    }
   }
 }
 
-#define CHAIN_W8_KERNEL(NAME, NBW, ACT)                                                       \
+#define CHAIN_W8_KERNEL(NAME, NBW, GATED, ACT)                                                \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
-  void NAME(const GemmParams p) { gemm_bf16_w8<NBW, ACT>(p); }
-#define CHAIN_W8_KERNELS(SUFFIX, ACT)                              \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_2_##SUFFIX, 2, ACT)          \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_3_##SUFFIX, 3, ACT)          \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_4_##SUFFIX, 4, ACT)
+  void NAME(const GemmParams p) { gemm_bf16_w8<NBW, GATED, ACT>(p); }
+#define CHAIN_W8_KERNELS(SUFFIX, ACT)                                    \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_2_##SUFFIX, 2, false, ACT)         \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_3_##SUFFIX, 3, false, ACT)         \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_4_##SUFFIX, 4, false, ACT)         \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_2_##SUFFIX, 2, true, ACT)    \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_4_##SUFFIX, 4, true, ACT)
 CHAIN_W8_KERNELS(erf, CHAIN_ACT_GELU_ERF)
 CHAIN_W8_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
 CHAIN_W8_KERNELS(id, CHAIN_ACT_IDENTITY)
@@ -800,6 +831,14 @@ void launch_bf16_width(const GemmParams &p, int nbw, hipStream_t stream) {
   else launch_bf16<2>(p, stream);
 }
 
+// The eight-wave kernels address a tile's rows with 32-bit byte offsets.
+bool w8_fits(const GemmParams &p, int nbw, bool gated) {
+  const int obn = gated ? 32 * nbw : 64 * nbw;   // output columns per tile
+  const int64_t span_a = ((int64_t)(min(p.M, BM) - 1) * p.lda + p.K) * 2;
+  const int64_t span_b = ((int64_t)(min(p.N, obn) - 1) * p.b_sn + p.K) * 2;
+  return span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
+}
+
 // Gated: 32 * nbw output columns per tile; nbw 4 unless 2 fills the chip's
 // rounds with less work per CU.
 void launch_dtl_gated(const GemmParams &p, int cus, hipStream_t stream) {
@@ -811,6 +850,14 @@ void launch_dtl_gated(const GemmParams &p, int cus, hipStream_t stream) {
   const int nbw = cost(2) < cost(4) ? 2 : 4;
   const int tiles = tm * ((p.N + 32 * nbw - 1) / (32 * nbw));
   typedef void (*Kern)(const GemmParams);
+  if (w8_fits(p, nbw, true)) {
+    static const Kern w2[4] = {gemm_bf16_w8_gated_kernel_2_erf, gemm_bf16_w8_gated_kernel_2_tanh,
+                               gemm_bf16_w8_gated_kernel_2_id, gemm_bf16_w8_gated_kernel_2_silu};
+    static const Kern w4[4] = {gemm_bf16_w8_gated_kernel_4_erf, gemm_bf16_w8_gated_kernel_4_tanh,
+                               gemm_bf16_w8_gated_kernel_4_id, gemm_bf16_w8_gated_kernel_4_silu};
+    hipLaunchKernelGGL((nbw == 4 ? w4 : w2)[p.act], dim3(tiles), dim3(512), 0, stream, p);
+    return;
+  }
   static const Kern k2[4] = {gemm_bf16_dtl_gated_kernel_2_erf, gemm_bf16_dtl_gated_kernel_2_tanh,
                              gemm_bf16_dtl_gated_kernel_2_id, gemm_bf16_dtl_gated_kernel_2_silu};
   static const Kern k4[4] = {gemm_bf16_dtl_gated_kernel_4_erf, gemm_bf16_dtl_gated_kernel_4_tanh,
@@ -836,13 +883,6 @@ void launch_w8(const GemmParams &p, int nbw, hipStream_t stream) {
       {gemm_bf16_w8_kernel_3_erf, gemm_bf16_w8_kernel_3_tanh, gemm_bf16_w8_kernel_3_id, gemm_bf16_w8_kernel_3_silu},
       {gemm_bf16_w8_kernel_4_erf, gemm_bf16_w8_kernel_4_tanh, gemm_bf16_w8_kernel_4_id, gemm_bf16_w8_kernel_4_silu}};
   hipLaunchKernelGGL(ks[nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
-}
-
-// The eight-wave kernel addresses a tile's rows with 32-bit byte offsets.
-bool w8_fits(const GemmParams &p, int nbw) {
-  const int64_t span_a = ((int64_t)(min(p.M, BM) - 1) * p.lda + p.K) * 2;
-  const int64_t span_b = ((int64_t)(min(p.N, 64 * nbw) - 1) * p.b_sn + p.K) * 2;
-  return span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
 }
 
 int compute_units() {
@@ -880,7 +920,7 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
   } else if (dtype == CHAIN_BF16) {
     const int nbw = gemm_bf16_block_cols(p.M, p.N, compute_units());
     if (p.b_sk == 1) {
-      if (w8_fits(p, nbw)) launch_w8(p, nbw, stream);
+      if (w8_fits(p, nbw, false)) launch_w8(p, nbw, stream);
       else launch_dtl(p, nbw, stream);
     } else {
       launch_bf16_width(p, nbw, stream);
