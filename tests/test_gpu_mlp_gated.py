@@ -55,6 +55,28 @@ def test_gated_mlp_ffn_shard_m16384_sampled():
     assert err <= TOL_BF16
 
 
+def test_gated_mlp_row_stride_beyond_32bit_tile_offsets():
+    """X rows 4.4 M elements apart: a 256-row tile of X spans more than 2^31 bytes, so the
+    gate/up product runs on the four-wave kernel (64-bit addresses) and H.Wd on the
+    eight-wave one; the result equals the contiguous call's bit for bit."""
+    dev = device()
+    M, K, N, K2, lda = 300, 128, 136, 96, 4_400_000
+    x, wg, wu, wd = gen_mlp_gated(M, K, N, K2, amp_x=1.0, amp_w=0.05, seed=86)
+    xd = x.to(dev)
+    wgd, wud, wdd = _kmajor(wg.to(dev)), _kmajor(wu.to(dev)), _kmajor(wd.to(dev))
+    announce(f"mlp_gated X row stride {lda} (tile span beyond 2^31 bytes)")
+    store = torch.zeros((M - 1) * lda + K, dtype=torch.bfloat16, device=dev)
+    xs = store.as_strided((M, K), (lda, 1))
+    xs.copy_(xd)
+    o = chain.mlp_gated_fwd(xs, wgd, wud, wdd, act="silu")
+    dense = chain.mlp_gated_fwd(xd, wgd, wud, wdd, act="silu")
+    torch.cuda.synchronize()
+    assert torch.equal(o, dense)
+    ref = oracle.mlp_gated(f64(x), f64(wg), f64(wu), f64(wd), "silu")
+    assert max_abs(f64(o), ref) <= TOL_BF16
+    del store, xs
+
+
 def test_gated_mlp_down_weight_layouts_agree():
     """Wd row- or column-major: the same products in the same k order."""
     dev = device()
