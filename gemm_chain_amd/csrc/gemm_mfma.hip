@@ -702,34 +702,55 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
       else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
     }
   };
+  // bf16 rows that take 16-byte stores: the two lane halves (same row) swap
+  // half of their groups, so that each lane holds 8 consecutive columns: lane
+  // half 0 columns 8g..8g+7 and lane half 1 columns 8(g+1)..8(g+1)+7, g = 0, 2.
+  const bool vec16 = !p.c_f32 && ((uintptr_t)p.c % 16 == 0) && (p.ldc % 8 == 0);
+  auto pack2 = [](float x, float y) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 w = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, w);
+  };
+  // v[4g + e] is the value of column col0 + 8g + 4 * h2 + e of row gm
+  auto store_block = [&](int gm, int col0, const f32x16 &v) {
+    if (vec16) {
+#pragma unroll
+      for (int g = 0; g < 4; g += 2) {
+        const auto x0 = __builtin_amdgcn_permlane32_swap(pack2(v[4 * g], v[4 * g + 1]),
+                                                         pack2(v[4 * g + 4], v[4 * g + 5]), false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(pack2(v[4 * g + 2], v[4 * g + 3]),
+                                                         pack2(v[4 * g + 6], v[4 * g + 7]), false, false);
+        const int gn = col0 + 8 * (g + h2);
+        if (gn < p.N) *(u32x4 *)((__bf16 *)p.c + (int64_t)gm * p.ldc + gn) = u32x4{x0[0], x1[0], x0[1], x1[1]};
+      }
+    } else {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int gn = col0 + 8 * r4 + 4 * h2;
+        if (gn < p.N) store4(gm, gn, f32x4{v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]});
+      }
+    }
+  };
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int gm = m0 + wm * 64 + i * 32 + l32;
+    const int gm = m0 + wm * 64 + i * 32 + l32;   // the same in both lane halves
     if (gm >= p.M) continue;
     if constexpr (GATED) {
 #pragma unroll
-      for (int u = 0; u < NBW / 2; ++u)
+      for (int u = 0; u < NBW / 2; ++u) {
+        f32x16 v;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int gn = n0 + wn * (WTN / 2) + u * 32 + 8 * r4 + 4 * h2;
-          if (gn >= p.N) continue;
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][2 * u][4 * r4 + e], ACT) * acc[i][2 * u + 1][4 * r4 + e];
-          store4(gm, gn, v);
-        }
+        for (int r = 0; r < 16; ++r) v[r] = activate(acc[i][2 * u][r], ACT) * acc[i][2 * u + 1][r];
+        store_block(gm, n0 + wn * (WTN / 2) + u * 32, v);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j)
+      for (int j = 0; j < NBW; ++j) {
+        f32x16 v;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
-          if (gn >= p.N) continue;
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
-          store4(gm, gn, v);
-        }
+        for (int r = 0; r < 16; ++r) v[r] = activate(acc[i][j][r], ACT);
+        store_block(gm, n0 + wn * WTN + j * 32, v);
+      }
     }
   }
 }

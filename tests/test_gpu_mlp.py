@@ -125,15 +125,21 @@ def test_mlp_row_stride_beyond_32bit_tile_offsets():
     del store, xs
 
 
+@pytest.mark.parametrize("w2_kmajor", [False, True])
+@pytest.mark.parametrize("pad", [2, 4])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_mlp_output_row_stride_not_vector_aligned(out_dtype):
-    """An output whose row stride is not a multiple of 4 elements (element stores)."""
+def test_mlp_output_row_stride_not_vector_aligned(out_dtype, pad, w2_kmajor):
+    """An output whose row stride is not a multiple of 4 elements (pad 2: element stores)
+    or, in bf16, of 8 elements (pad 4: 8-byte stores instead of 16-byte ones), written by
+    the row-major-weight kernel or (W2 k-major) the eight-wave kernel."""
     dev = device()
     M, K, N, K2 = 260, 128, 136, 200
     x, w1, w2 = gen_mlp(M, K, N, K2, dtype="bf16", amp_x=1.0, amp_w=0.05, seed=70)
     xd, w1d, w2d = x.to(dev), _kmajor(w1.to(dev)), w2.to(dev)
-    announce(f"mlp strided output {out_dtype}")
-    base = torch.full((M, K2 + 2), 7.0, dtype=out_dtype, device=dev)
+    if w2_kmajor:
+        w2d = _kmajor(w2d)
+    announce(f"mlp strided output {out_dtype} pad {pad} w2_kmajor {w2_kmajor}")
+    base = torch.full((M, K2 + pad), 7.0, dtype=out_dtype, device=dev)
     o = base[:, :K2]
     chain.mlp_fwd(xd, w1d, w2d, act="gelu_tanh", out=o)
     dense = chain.mlp_fwd(xd, w1d, w2d, act="gelu_tanh", out_dtype=out_dtype)
