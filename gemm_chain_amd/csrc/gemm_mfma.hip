@@ -83,17 +83,85 @@ constexpr int LDA = BK + 8;        // pitch of k-contiguous stages
 
 __device__ inline u32x4 ld16(const __bf16 *p) { return *(const u32x4 *)p; }
 
+// Epilogue of a wave's MI x NBW grid of 32 x 32 blocks (rows r0 + 32 i + l32,
+// columns c0 + 32 j + 8 (r / 4) + 4 h2 + r % 4 in element r of acc[i][j]):
+// act(), then stores.  GATED: blocks 2j and 2j + 1 are the gate and up
+// products of output block j, which takes act(gate) * up.  bf16 rows that allow it take 16-byte stores: the two
+// lane halves (same row) swap half of their 4-column groups, so that each lane
+// holds 8 consecutive columns (half 0: 8g..8g+7, half 1: 8(g+1)..8(g+1)+7, for
+// g = 0, 2); otherwise 4 columns at a time.
+template <int MI, int NBW, bool GATED, int ACT>
+__device__ __forceinline__ void gemm_store_tile(const GemmParams &p, const f32x16 (&acc)[MI][NBW], int r0,
+                                                int c0, int l32, int h2) {
+  constexpr int NOB = GATED ? NBW / 2 : NBW;   // 32-column output blocks
+  const bool vec16 = !p.c_f32 && ((uintptr_t)p.c % 16 == 0) && (p.ldc % 8 == 0);
+  auto pack2 = [](float x, float y) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 w = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, w);
+  };
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int gm = r0 + i * 32 + l32;   // the same in both lane halves
+    if (gm >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < NOB; ++j) {
+      f32x16 v;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        v[r] = GATED ? activate(acc[i][2 * j][r], ACT) * acc[i][2 * j + 1][r] : activate(acc[i][j][r], ACT);
+      const int col0 = c0 + j * 32;
+      if (vec16) {
+#pragma unroll
+        for (int g = 0; g < 4; g += 2) {
+          const auto x0 = __builtin_amdgcn_permlane32_swap(pack2(v[4 * g], v[4 * g + 1]),
+                                                           pack2(v[4 * g + 4], v[4 * g + 5]), false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(pack2(v[4 * g + 2], v[4 * g + 3]),
+                                                           pack2(v[4 * g + 6], v[4 * g + 7]), false, false);
+          const int gn = col0 + 8 * (g + h2);
+          if (gn < p.N)
+            *(u32x4 *)((__bf16 *)p.c + (int64_t)gm * p.ldc + gn) = u32x4{x0[0], x1[0], x0[1], x1[1]};
+        }
+      } else {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int gn = col0 + 8 * r4 + 4 * h2;
+          if (gn >= p.N) continue;   // N % 4 == 0: the four columns are all in or all out
+          const f32x4 w4 = {v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]};
+          const int64_t off = (int64_t)gm * p.ldc + gn;
+          if (p.c_f32) {
+            float *c = (float *)p.c + off;
+            if (p.c_vec) *(f32x4 *)c = w4;
+            else c[0] = w4[0], c[1] = w4[1], c[2] = w4[2], c[3] = w4[3];
+          } else {
+            __bf16 *c = (__bf16 *)p.c + off;
+            const bf16x4 w = {(__bf16)w4[0], (__bf16)w4[1], (__bf16)w4[2], (__bf16)w4[3]};
+            if (p.c_vec) *(bf16x4 *)c = w;
+            else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
+          }
+        }
+      }
+    }
+  }
+}
+
 // n-contiguous B (row-major [K, N] weights).  NBW = 32-column blocks per wave
 // (BN = 64 * NBW).  ACT: the epilogue's activation, one instantiation each (a
 // run-time choice among several epilogues costs registers in the main loop).
+// Eight waves (two per SIMD) of 64 x BN/2 share the tile.  k-tiles of 64 are
+// staged through registers into two LDS buffers (A as [256][64 + 8], B as
+// [64][BN' + 32] read with ds_read_b64_tr_b16); the fetch of tile k+2 is issued
+// once tile k+1 is written to LDS.
 template <int NBW, int ACT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(const GemmParams p) {
+  constexpr int NW = 8, NT = 64 * NW;                    // waves, threads
+  constexpr int WMR = BM / (NW / 2), MI = WMR / 32;      // rows per wave, 32-row blocks per wave
   constexpr int BN = 64 * NBW, WTN = 32 * NBW;
   constexpr int LDBN = ((BN + 127) / 128) * 128 + 32;   // B pitch: conflict-free tr reads
   constexpr int BSZ = BK * LDBN;
-  constexpr int AL = BM * BK / 8 / 256;                  // 16-byte chunks per thread
-  constexpr int BL = BN * BK / 8 / 256;
+  constexpr int AL = BM * BK / 8 / NT;                   // 16-byte chunks per thread
+  constexpr int BL = BN * BK / 8 / NT;
   constexpr int BCH = BN / 8;                            // chunks per B row
   __shared__ __attribute__((aligned(16))) __bf16 as[2][BM * LDA];
   __shared__ __attribute__((aligned(16))) __bf16 bs[2][BSZ];
@@ -111,7 +179,7 @@ void gemm_bf16_kernel(const GemmParams p) {
   const int nk = (p.K + BK - 1) / BK;
   const int nk_plain = (m0 + BM <= p.M && n0 + BN <= p.N) ? p.K / BK : 0;
 
-  // Chunk c = tid + 256 i of a stage: A row (c >> 3) = (tid >> 3) + 32 i, k
+  // Chunk c = tid + NT i of a stage: A row (c >> 3) = (tid >> 3) + (NT / 8) i, k
   // chunk c & 7 = tid & 7; a B row holds BCH chunks.  Per-thread byte offsets
   // stay 32-bit; the per-i part is uniform.
   const char *Ab = (const char *)A, *Bb = (const char *)B;
@@ -123,14 +191,14 @@ void gemm_bf16_kernel(const GemmParams p) {
     if (kt < nk_plain) {
 #pragma unroll
       for (int i = 0; i < AL; ++i) {
-        const char *base = Ab + ((int64_t)(m0 + 32 * i) * p.lda + k0) * 2;
+        const char *base = Ab + ((int64_t)(m0 + (NT / 8) * i) * p.lda + k0) * 2;
         ar[i] = *(const u32x4 *)(base + a_off);
       }
 #pragma unroll
       for (int i = 0; i < BL; ++i) {
-        const int c = tid + 256 * i;
-        if (256 % BCH == 0) {
-          const char *base = Bb + ((int64_t)(k0 + (256 / BCH) * i) * ldb + n0) * 2;
+        const int c = tid + NT * i;
+        if (NT % BCH == 0) {
+          const char *base = Bb + ((int64_t)(k0 + (NT / BCH) * i) * ldb + n0) * 2;
           br[i] = *(const u32x4 *)(base + b_off);
         } else {
           br[i] = ld16(B + (int64_t)(k0 + c / BCH) * ldb + n0 + (c % BCH) * 8);
@@ -140,7 +208,7 @@ void gemm_bf16_kernel(const GemmParams p) {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < AL; ++i) {
-        const int c = tid + 256 * i;
+        const int c = tid + NT * i;
         const int gm = m0 + (c >> 3), gk = k0 + (c & 7) * 8;
         const bool ok = gm < p.M && gk < p.K;
         const u32x4 v = ld16(ok ? A + (int64_t)gm * p.lda + gk : A);
@@ -148,7 +216,7 @@ void gemm_bf16_kernel(const GemmParams p) {
       }
 #pragma unroll
       for (int i = 0; i < BL; ++i) {
-        const int c = tid + 256 * i;
+        const int c = tid + NT * i;
         const int gk = k0 + c / BCH, gn = n0 + (c % BCH) * 8;
         const bool ok = gk < p.K && gn < p.N;
         const u32x4 v = ld16(ok ? B + (int64_t)gk * ldb + gn : B);
@@ -159,25 +227,25 @@ void gemm_bf16_kernel(const GemmParams p) {
   auto swrite = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       *(u32x4 *)(&as[buf][(c >> 3) * LDA + (c & 7) * 8]) = ar[i];
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       *(u32x4 *)(&bs[buf][(c / BCH) * LDBN + (c % BCH) * 8]) = br[i];
     }
   };
 
   struct Frags {
-    bf16x8 a[4], b[NBW];
+    bf16x8 a[MI], b[NBW];
   };
   const int trow = (lane & 15) >> 2;
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   auto frags = [&](int buf, int ks, Frags &f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f.a[i] = *(const bf16x8 *)(&as[buf][(wm * 128 + i * 32 + l32) * LDA + ks * 16 + 8 * h2]);
+    for (int i = 0; i < MI; ++i)
+      f.a[i] = *(const bf16x8 *)(&as[buf][(wm * WMR + i * 32 + l32) * LDA + ks * 16 + 8 * h2]);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const __bf16 *src = &bs[buf][(ks * 16 + 8 * h2 + trow) * LDBN + wn * WTN + j * 32 + tcol];
@@ -189,81 +257,43 @@ void gemm_bf16_kernel(const GemmParams p) {
 
   // acc[i][j] holds the transposed 32 x 32 block: lane (h2, l32) has row
   // m = l32 and columns n = 8 * (r / 4) + 4 * h2 + r % 4 in element r.
-  f32x16 acc[4][NBW];
+  f32x16 acc[MI][NBW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = f32x16{};
   auto mfmas = [&](const Frags &f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
 
-  Frags f0, f1;
+  Frags f0;
   if (nk > 0) {   // K = 0: nothing to load (the operands may have no storage)
     gload(0);
     swrite(0);
     if (nk > 1) gload(1);
     __syncthreads();
-    frags(0, 0, f0);
   }
+  // One fragment set per wave (the other wave on the SIMD covers the read
+  // latency), which keeps the 64 x 256 wave tile within 256 registers.
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1, nxt = cur ^ 1;
-    frags(cur, 1, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0);
-    __builtin_amdgcn_sched_barrier(0);
-    frags(cur, 2, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      swrite(nxt);
-      if (kt + 2 < nk) gload(kt + 2);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      frags(cur, ks, f0);
+      mfmas(f0);
+      if (ks == 1 && kt + 1 < nk) {
+        swrite(nxt);
+        if (kt + 2 < nk) gload(kt + 2);
+      }
     }
-    frags(cur, 3, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0);
-    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    if (kt + 1 < nk) frags(nxt, 0, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1);
-    __builtin_amdgcn_sched_barrier(0);
   }
 
-  auto store_all = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gm = m0 + wm * 128 + i * 32 + l32;
-      if (gm >= p.M) continue;
-#pragma unroll
-      for (int j = 0; j < NBW; ++j)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int gn = n0 + wn * WTN + j * 32 + 8 * r4 + 4 * h2;
-          if (gn >= p.N) continue;   // N % 4 == 0: the four columns are all in or all out
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = activate(acc[i][j][4 * r4 + e], ACT);
-          const int64_t off = (int64_t)gm * p.ldc + gn;
-          if (p.c_f32) {
-            float *c = (float *)p.c + off;
-            if (p.c_vec) *(f32x4 *)c = v;
-            else c[0] = v[0], c[1] = v[1], c[2] = v[2], c[3] = v[3];
-          } else {
-            __bf16 *c = (__bf16 *)p.c + off;
-            const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-            if (p.c_vec) *(bf16x4 *)c = w;
-            else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
-          }
-        }
-    }
-  };
-  store_all();
+  gemm_store_tile<MI, NBW, false, ACT>(p, acc, m0 + wm * WMR, n0 + wn * WTN, l32, h2);
 }
 
 // ---- k-contiguous A and B: direct-to-LDS stage ring ------------------------
@@ -689,70 +719,7 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
     wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
   }
 
-  auto store4 = [&](int gm, int gn, const f32x4 &v) {
-    const int64_t off = (int64_t)gm * p.ldc + gn;
-    if (p.c_f32) {
-      float *c = (float *)p.c + off;
-      if (p.c_vec) *(f32x4 *)c = v;
-      else c[0] = v[0], c[1] = v[1], c[2] = v[2], c[3] = v[3];
-    } else {
-      __bf16 *c = (__bf16 *)p.c + off;
-      const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-      if (p.c_vec) *(bf16x4 *)c = w;
-      else c[0] = w[0], c[1] = w[1], c[2] = w[2], c[3] = w[3];
-    }
-  };
-  // bf16 rows that take 16-byte stores: the two lane halves (same row) swap
-  // half of their groups, so that each lane holds 8 consecutive columns: lane
-  // half 0 columns 8g..8g+7 and lane half 1 columns 8(g+1)..8(g+1)+7, g = 0, 2.
-  const bool vec16 = !p.c_f32 && ((uintptr_t)p.c % 16 == 0) && (p.ldc % 8 == 0);
-  auto pack2 = [](float x, float y) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 w = {(__bf16)x, (__bf16)y};
-    return __builtin_bit_cast(uint32_t, w);
-  };
-  // v[4g + e] is the value of column col0 + 8g + 4 * h2 + e of row gm
-  auto store_block = [&](int gm, int col0, const f32x16 &v) {
-    if (vec16) {
-#pragma unroll
-      for (int g = 0; g < 4; g += 2) {
-        const auto x0 = __builtin_amdgcn_permlane32_swap(pack2(v[4 * g], v[4 * g + 1]),
-                                                         pack2(v[4 * g + 4], v[4 * g + 5]), false, false);
-        const auto x1 = __builtin_amdgcn_permlane32_swap(pack2(v[4 * g + 2], v[4 * g + 3]),
-                                                         pack2(v[4 * g + 6], v[4 * g + 7]), false, false);
-        const int gn = col0 + 8 * (g + h2);
-        if (gn < p.N) *(u32x4 *)((__bf16 *)p.c + (int64_t)gm * p.ldc + gn) = u32x4{x0[0], x1[0], x0[1], x1[1]};
-      }
-    } else {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int gn = col0 + 8 * r4 + 4 * h2;
-        if (gn < p.N) store4(gm, gn, f32x4{v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]});
-      }
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int gm = m0 + wm * 64 + i * 32 + l32;   // the same in both lane halves
-    if (gm >= p.M) continue;
-    if constexpr (GATED) {
-#pragma unroll
-      for (int u = 0; u < NBW / 2; ++u) {
-        f32x16 v;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = activate(acc[i][2 * u][r], ACT) * acc[i][2 * u + 1][r];
-        store_block(gm, n0 + wn * (WTN / 2) + u * 32, v);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        f32x16 v;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = activate(acc[i][j][r], ACT);
-        store_block(gm, n0 + wn * WTN + j * 32, v);
-      }
-    }
-  }
+  gemm_store_tile<2, NBW, GATED, ACT>(p, acc, m0 + wm * 64, n0 + wn * (GATED ? WTN / 2 : WTN), l32, h2);
 }
 
 #define CHAIN_W8_KERNEL(NAME, NBW, GATED, ACT)                                                \
@@ -838,11 +805,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams p) {
 template <int NBW>
 void launch_bf16(const GemmParams &p, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * NBW - 1) / (64 * NBW));
+  const dim3 grid(tiles), block(512);
   switch (p.act) {
-    case CHAIN_ACT_GELU_ERF: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_GELU_ERF>), dim3(tiles), dim3(256), 0, stream, p); break;
-    case CHAIN_ACT_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_GELU_TANH>), dim3(tiles), dim3(256), 0, stream, p); break;
-    case CHAIN_ACT_SILU: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_SILU>), dim3(tiles), dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_IDENTITY>), dim3(tiles), dim3(256), 0, stream, p);
+    case CHAIN_ACT_GELU_ERF: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_GELU_ERF>), grid, block, 0, stream, p); break;
+    case CHAIN_ACT_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_GELU_TANH>), grid, block, 0, stream, p); break;
+    case CHAIN_ACT_SILU: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_SILU>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((gemm_bf16_kernel<NBW, CHAIN_ACT_IDENTITY>), grid, block, 0, stream, p);
   }
 }
 
