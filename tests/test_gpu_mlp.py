@@ -37,12 +37,17 @@ def test_mlp_small_full_compare(M, K, N, K2, dtype, act, out):
     assert err <= tol
 
 
-def test_mlp_ffn_shard_m16384_sampled():
+@pytest.mark.parametrize("kmajor", [False, True])
+def test_mlp_ffn_shard_m16384_sampled(kmajor):
+    """Full size, with the weights row-major or (as the bench times them) k-major."""
     w = WORKLOADS["mlp_bf16_m16384_k4096_n1376"]
     dev = device()
     x, w1, w2 = gen_mlp(w.M, w.K, w.N, dtype=w.dtype, amp_x=w.amp_x, amp_w=w.amp_w, seed=w.seed)
-    announce("mlp 16384x4096x1376 full size")
-    o = chain.mlp_fwd(x.to(dev), w1.to(dev), w2.to(dev), act=w.act)
+    announce(f"mlp 16384x4096x1376 full size kmajor={kmajor}")
+    w1d, w2d = w1.to(dev), w2.to(dev)
+    if kmajor:
+        w1d, w2d = _kmajor(w1d), _kmajor(w2d)
+    o = chain.mlp_fwd(x.to(dev), w1d, w2d, act=w.act)
     torch.cuda.synchronize()
     rows = sample_rows(w.M, 160, w.seed, extra=(127, 128, 8191))
     ref = oracle.mlp(f64(x[rows]), f64(w1), f64(w2), w.act)
