@@ -169,10 +169,14 @@ void gemm_bf16_kernel(const GemmParams p) {
   const int h2 = lane >> 5, l32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const int tiles_n = (p.N + BN - 1) / BN;
-  const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
-  const int tile = xcd_remap(blockIdx.x, tiles);
-  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  // Tile order: groups of 4 row blocks x all column blocks, row block fastest,
+  // so the 32 tiles an XCD runs at once cover 4 x 8 blocks.
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  constexpr int GM = 4;
+  const int g = t / (GM * tiles_n), fm = g * GM;
+  const int gmn = min(GM, tiles_m - fm), loc = t - g * GM * tiles_n;
+  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * BN;
   const __bf16 *A = (const __bf16 *)p.a;
   const __bf16 *B = (const __bf16 *)p.b;
   const int64_t ldb = p.b_sk;
