@@ -58,19 +58,42 @@ def attn_flops(B, Hq, Sq, Sk, D, causal=True):
     return f / 2 if causal else f
 
 
-def time_region(torch, fn, steps, warmup, stream):
-    """Mean ms per call of fn over `steps` calls, HIP events on `stream`."""
+def time_region(torch, fn, steps, warmup, stream, per_step=None):
+    """Mean ms per call of fn over `steps` calls, HIP events on `stream`.  If
+    per_step is a list, the duration of each call (events between the calls of
+    the same timed region) is appended to it."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(stream)
+    for i in range(steps):
         fn()
-    end.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    if per_step is not None:
+        per_step.extend(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    return marks[0].elapsed_time(marks[-1]) / steps
+
+
+def spread(ms):
+    """median, p10 and p90 of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def device_record(torch):
+    """What the numbers were measured on."""
+    props = torch.cuda.get_device_properties(0)
+    rec = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count,
+           "memory_gib": round(props.total_memory / 2**30, 1), "rocm": torch.version.hip}
+    clock = getattr(props, "clock_rate", None)
+    if clock:
+        rec["clock_mhz"] = round(clock / 1000)
+    return rec
 
 
 def headline(torch, chain, steps, warmup):
@@ -88,9 +111,10 @@ def headline(torch, chain, steps, warmup):
         chain.attn_fwd(qd, kd, vd, causal=True, n_chunks=w.n_chunks, zigzag=w.zigzag, out=o, lse=lse)
 
     log(f"timing {steps} steps after {warmup} warmup")
-    ms = time_region(torch, step, steps, warmup, stream)
+    per_step = []
+    ms = time_region(torch, step, steps, warmup, stream, per_step)
     flops = attn_flops(w.B, w.Hq, w.S, w.S, w.D)
-    return w, (q, k, v), ms, flops
+    return w, (q, k, v), ms, flops, per_step
 
 
 def cpu_baseline(w, inputs, budget_s=12.0):
@@ -258,7 +282,7 @@ def main():
     import torch
     from gemm_chain_amd import chain
     chain.load()
-    w, inputs, ms, flops = headline(torch, chain, args.steps, args.warmup)
+    w, inputs, ms, flops, per_step = headline(torch, chain, args.steps, args.warmup)
     tflops = flops / ms / 1e9
     log(f"{w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
     record = {
@@ -282,6 +306,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": committed_traffic()},
+        "step_ms": spread(per_step),
+        "device": device_record(torch),
     }
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0").fill_(1)
