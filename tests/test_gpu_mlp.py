@@ -89,6 +89,8 @@ def _kmajor(w):
     (16000, 4096, 1376, 4096),
     (4000, 1376, 4096, 264),
     (300, 200, 136, 264),
+    (96, 8, 24, 40),            # K and N below one 32-deep stage: only K-tail stages
+    (33, 40, 8, 16),            # one partial row tile, one 8-column inner block
 ])
 def test_mlp_weight_layouts_agree_and_match_oracle(M, K, N, K2):
     dev = device()
