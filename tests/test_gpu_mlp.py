@@ -90,6 +90,7 @@ def _kmajor(w):
     (4000, 1376, 4096, 264),
     (300, 200, 136, 264),
     (96, 8, 24, 40),            # K and N below one 32-deep stage: only K-tail stages
+    (16000, 4008, 1376, 264),   # 192-wide tiles (uneven loads of B per wave) with a K tail
     (33, 40, 8, 16),            # one partial row tile, one 8-column inner block
 ])
 def test_mlp_weight_layouts_agree_and_match_oracle(M, K, N, K2):
