@@ -26,6 +26,7 @@ def _kmajor(w):
     (300, 256, 136, 264, "identity", "f32"),   # f32 output: no output rounding
     (257, 4096, 1376, 512, "silu", None),      # gated FFN shard inner width, full K
     (64, 64, 8, 64, "silu", "f32"),            # a single 8-column inner block
+    (300, 136, 264, 200, "silu", None),        # K tail in the gate/up product, N and K2 ragged
 ])
 def test_gated_mlp_small_full_compare(M, K, N, K2, act, out):
     dev = device()
