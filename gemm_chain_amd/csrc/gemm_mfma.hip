@@ -281,20 +281,51 @@ void gemm_bf16_kernel(const GemmParams p) {
     if (nk > 1) gload(1);
     __syncthreads();
   }
-  // One fragment set per wave (the other wave on the SIMD covers the read
-  // latency), which keeps the 64 x 256 wave tile within 256 registers.
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
+  if constexpr (NBW == 4) {
+    // One fragment set per wave (the other wave on the SIMD covers the read
+    // latency), which keeps the 64 x 256 wave tile within 256 registers.
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1, nxt = cur ^ 1;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      frags(cur, ks, f0);
+      for (int ks = 0; ks < 4; ++ks) {
+        frags(cur, ks, f0);
+        mfmas(f0);
+        if (ks == 1 && kt + 1 < nk) {
+          swrite(nxt);
+          if (kt + 2 < nk) gload(kt + 2);
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // Narrower tiles leave room for two fragment sets: each k-step's fragments
+    // are read while the previous k-step's MFMAs run.
+    Frags f1;
+    if (nk > 0) frags(0, 0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1, nxt = cur ^ 1;
+      frags(cur, 1, f1);
+      __builtin_amdgcn_sched_barrier(0);
       mfmas(f0);
-      if (ks == 1 && kt + 1 < nk) {
+      __builtin_amdgcn_sched_barrier(0);
+      frags(cur, 2, f0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) {
         swrite(nxt);
         if (kt + 2 < nk) gload(kt + 2);
       }
+      frags(cur, 3, f1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      if (kt + 1 < nk) frags(nxt, 0, f0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
   }
 
   gemm_store_tile<MI, NBW, false, ACT>(p, acc, m0 + wm * WMR, n0 + wn * WTN, l32, h2);
