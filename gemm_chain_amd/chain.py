@@ -70,6 +70,7 @@ def load():
         "chain_lse_merge": (ctypes.c_int, [T, T, T, T, vp]),
         "chain_mlp_fwd": (ctypes.c_int, [T, T, T, T, ctypes.c_int, vp, sz, vp]),
         "chain_mlp_workspace_bytes": (sz, [i64, i64, i32]),
+        "chain_mlp_fwd_noalloc": (ctypes.c_int, [T, T, T, T, ctypes.c_int, vp]),
         "chain_mlp_gated_fwd": (ctypes.c_int, [T, T, T, T, T, ctypes.c_int, vp, sz, vp]),
         "chain_attn_bwd": (ctypes.c_int, [T, T, T, T, T, T, T, T, T, ctypes.c_int, f32, vp, sz, vp]),
         "chain_attn_bwd_workspace_bytes": (sz, [i64, i64, i64]),
@@ -228,6 +229,16 @@ def mlp_fwd(x, w1, w2, act="gelu_erf", out=None, out_dtype=None, workspace=None)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _check(lib.chain_mlp_fwd(desc(x), desc(w1), desc(w2), desc(o), ACTS[act],
                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(x)))
+    return o
+
+
+def mlp_fwd_noalloc(x, w1, w2, act="gelu_erf", out=None, out_dtype=None):
+    """O = act(X.W1).W2 with the intermediate in the library's static device scratch
+    (no workspace; the library allocates nothing)."""
+    lib = load()
+    M, K2 = x.shape[0], w2.shape[1]
+    o = torch.empty((M, K2), dtype=out_dtype or x.dtype, device=x.device) if out is None else out
+    _check(lib.chain_mlp_fwd_noalloc(desc(x), desc(w1), desc(w2), desc(o), ACTS[act], _stream(x)))
     return o
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -306,9 +307,43 @@ size_t chain_mlp_workspace_bytes(int64_t M, int64_t N, int32_t dt) {
   return (b + 255) / 256 * 256;
 }
 
-chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const chain_tensor *W2,
-                           const chain_tensor *O, int act, void *workspace, size_t ws_bytes,
-                           void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Device scratch of chain_mlp_fwd_noalloc: one copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it names a stand-in, not device memory); it uses the device address
+// hipGetSymbolAddress returns for the current device, fetched once per device.
+__device__ __align__(256) unsigned char scratch[CHAIN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+chain_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CHAIN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CHAIN_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(CHAIN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CHAIN_OK;
+}
+
+// chain_mlp_fwd's body.  With noalloc the caller's workspace arguments are
+// ignored: H goes to this device's static scratch, and shapes whose H does not
+// fit it are refused before anything else happens.
+chain_status mlp_fwd_impl(const chain_tensor *X, const chain_tensor *W1, const chain_tensor *W2,
+                          const chain_tensor *O, int act, void *workspace, size_t ws_bytes,
+                          void *stream, bool noalloc) {
   TRY(check_tensor(X, "X", 2));
   TRY(check_tensor(W1, "W1", 2, 16, true));
   TRY(check_tensor(W2, "W2", 2, 16, true));
@@ -326,7 +361,14 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
   if (overlap(*O, *X) || overlap(*O, *W1) || overlap(*O, *W2))
     return fail(CHAIN_ERR_ALIAS, "O overlaps an input");
   const size_t need = chain_mlp_workspace_bytes(M, N, X->dtype);
+  if (noalloc && need > CHAIN_NOALLOC_SCRATCH_BYTES)
+    return fail(CHAIN_ERR_WORKSPACE, "H of %lld x %lld needs %zu bytes; the static scratch holds %zu",
+                (long long)M, (long long)N, need, (size_t)CHAIN_NOALLOC_SCRATCH_BYTES);
   if (M == 0 || K2 == 0) return ok();
+  if (noalloc) {
+    TRY(scratch_address(&workspace));
+    ws_bytes = CHAIN_NOALLOC_SCRATCH_BYTES;
+  }
   if (workspace == nullptr || ws_bytes < need)
     return fail(CHAIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if ((uintptr_t)workspace % 256) return fail(CHAIN_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -370,6 +412,21 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const 
   if (e == hipSuccess) e = chain::launch_gemm(g2, X->dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(CHAIN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1, const chain_tensor *W2,
+                           const chain_tensor *O, int act, void *workspace, size_t ws_bytes,
+                           void *stream) {
+  return mlp_fwd_impl(X, W1, W2, O, act, workspace, ws_bytes, stream, false);
+}
+
+chain_status chain_mlp_fwd_noalloc(const chain_tensor *X, const chain_tensor *W1, const chain_tensor *W2,
+                                   const chain_tensor *O, int act, void *stream) {
+  return mlp_fwd_impl(X, W1, W2, O, act, nullptr, 0, stream, true);
 }
 
 size_t chain_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t S) {

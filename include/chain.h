@@ -29,7 +29,8 @@
  * - Memory: every tensor's data lives in device memory of the current HIP
  *   device; the caller allocates and owns all of it (including the MLP
  *   workspace).  The library never allocates or frees device memory and keeps
- *   no state between calls other than a thread-local error message.
+ *   no state between calls other than a thread-local error message, except
+ *   chain_mlp_fwd_noalloc's static per-GPU scratch (described there).
  * - Layout: chain_tensor gives shape and strides in ELEMENTS; the last
  *   dimension must be contiguous (stride 1), other strides are free (>= 0);
  *   the MLP weights may instead have their first dimension contiguous.
@@ -206,6 +207,32 @@ chain_status chain_mlp_fwd(const chain_tensor *X, const chain_tensor *W1,
 /* Bytes of workspace chain_mlp_fwd needs for an M x N intermediate of dtype
  * dt (a chain_dtype), rounded up to 256.  0 for an invalid dtype. */
 size_t chain_mlp_workspace_bytes(int64_t M, int64_t N, int32_t dt);
+
+/* Size of the static device scratch behind chain_mlp_fwd_noalloc: 64 MiB on
+ * each GPU the library runs the call on, held until the process ends. */
+#define CHAIN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * chain_mlp_fwd_noalloc -- chain_mlp_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, kernels and results as
+ * chain_mlp_fwd, without the workspace: H = act(X.W1) lives in a static
+ * device array of CHAIN_NOALLOC_SCRATCH_BYTES per GPU.
+ *
+ *   X, W1, W2, O, act, stream   as for chain_mlp_fwd
+ * The call allocates nothing (no hipMalloc, no library allocation).  The
+ * first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, current device); a failure there returns
+ * CHAIN_ERR_HIP.  Shapes whose H needs more than CHAIN_NOALLOC_SCRATCH_BYTES
+ * (chain_mlp_workspace_bytes(M, N, dtype)) return CHAIN_ERR_WORKSPACE before
+ * anything runs; for bf16 that is M * N <= 32 Mi elements.  Every call on a
+ * GPU shares that GPU's array, which keeps the last call's H: calls that
+ * overlap on one GPU (different streams, or threads without ordering) race
+ * and give wrong results.  Calls ordered on one stream are safe.
+ */
+chain_status chain_mlp_fwd_noalloc(const chain_tensor *X, const chain_tensor *W1,
+                                   const chain_tensor *W2, const chain_tensor *O, int act,
+                                   void *stream);
 
 /*
  * chain_mlp_gated_fwd -- O = (act(X.Wg) * (X.Wu)).Wd, * elementwise: the gated MLP

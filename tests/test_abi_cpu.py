@@ -378,3 +378,30 @@ def test_linear_attn_validation_codes(lib):
              v=td([1, 2, 0, 128], chain.BF16, FAKE + 2 * G), o=td([1, 4, 0, 128], chain.F32, FAKE + 3 * G),
              si=None, so=None, w=None, n=0)
     assert call(**E) == CODES["CHAIN_OK"]
+
+
+def test_mlp_noalloc_refuses_before_touching_the_device(lib):
+    """Shapes whose intermediate exceeds the static scratch, and invalid
+    arguments, fail validation before the call looks up any device memory."""
+    P = ctypes.byref
+    M, K, N = 8200, 8, 4096                  # H = 67,174,400 bytes > 64 MiB
+    X = td([M, K], chain.BF16, FAKE)
+    W1 = td([K, N], chain.BF16, FAKE + 2 ** 30)
+    W2 = td([N, K], chain.BF16, FAKE + 2 * 2 ** 30)
+    O = td([M, K], chain.BF16, FAKE + 3 * 2 ** 30)
+    assert lib.chain_mlp_workspace_bytes(M, N, chain.BF16) > 64 * 2 ** 20
+    assert lib.chain_mlp_fwd_noalloc(P(X), P(W1), P(W2), P(O), 0, None) == CODES["CHAIN_ERR_WORKSPACE"]
+    assert b"static scratch" in lib.chain_last_error()
+    Xs = td([512, 256], chain.BF16, FAKE)
+    W1s = td([256, 128], chain.BF16, FAKE + 2 ** 30)
+    W2s = td([128, 256], chain.BF16, FAKE + 2 * 2 ** 30)
+    Os = td([512, 256], chain.BF16, FAKE + 3 * 2 ** 30)
+    assert lib.chain_mlp_fwd_noalloc(P(Xs), P(W1s), P(W2s), P(Os), 7, None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    W1f = td([256, 128], chain.F32, FAKE + 2 ** 30)
+    assert lib.chain_mlp_fwd_noalloc(P(Xs), P(W1f), P(W2s), P(Os), 0, None) == CODES["CHAIN_ERR_DTYPE"]
+    Oal = td([512, 256], chain.BF16, FAKE + 256)
+    assert lib.chain_mlp_fwd_noalloc(P(Xs), P(W1s), P(W2s), P(Oal), 0, None) == CODES["CHAIN_ERR_ALIAS"]
+    # an empty product is valid and touches nothing
+    X0 = td([0, 256], chain.BF16, FAKE)
+    O0 = td([0, 256], chain.BF16, FAKE + 3 * 2 ** 30)
+    assert lib.chain_mlp_fwd_noalloc(P(X0), P(W1s), P(W2s), P(O0), 0, None) == CODES["CHAIN_OK"]
