@@ -6,8 +6,12 @@ binding; importing this package does not load the library, the first call
 does, and it raises if the library is missing.
 """
 
-from .chain import (ChainError, attn_fwd, attn_partial, lse_merge, mlp_fwd,
-                    mlp_workspace_bytes, tile_census, zigzag_segments, library_path, load)
+from .chain import (ChainError, attn_bwd, attn_bwd_workspace_bytes, attn_fwd, attn_partial,
+                    library_path, linear_attn_fwd, linear_attn_workspace_bytes, load, lse_merge,
+                    mlp_fwd, mlp_fwd_noalloc, mlp_gated_fwd, mlp_workspace_bytes, tile_census,
+                    zigzag_segments)
 
-__all__ = ["ChainError", "attn_fwd", "attn_partial", "lse_merge", "mlp_fwd",
-           "mlp_workspace_bytes", "tile_census", "zigzag_segments", "library_path", "load"]
+__all__ = ["ChainError", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_partial",
+           "library_path", "linear_attn_fwd", "linear_attn_workspace_bytes", "load", "lse_merge",
+           "mlp_fwd", "mlp_fwd_noalloc", "mlp_gated_fwd", "mlp_workspace_bytes", "tile_census",
+           "zigzag_segments"]
