@@ -18,19 +18,29 @@
 // holds keys {4h..4h+3, 8+4h..8+4h+3}, and the V^T operand is read in that
 // order from the row-major V tile with ds_read_b64_tr_b16.
 //
-// Eight waves per workgroup (two per SIMD) share each staged 64-key K/V tile.
+// Eight waves per workgroup (two per SIMD: waves w and w+4) share each staged
+// 64-key K/V tile.  They run a ping-pong schedule: every wave alternates an
+// MFMA phase (K.Q^T of tile j, then P.V of tile j-1) and a softmax phase (tile
+// j), waves 4-7 one phase behind waves 0-3, with a workgroup barrier between
+// phases, so on each SIMD one wave's MFMA run meets the other wave's softmax.
 // Tiles reach LDS by buffer loads that write LDS directly (64 lanes x 16 bytes
 // per wave-level load, no staging registers, no LDS write instructions) into a
-// ring of four stages fetched three tiles ahead; one barrier per tile.  Staged
-// rows are not padded: 16-byte chunks are XOR-swizzled per row so that the
-// 16-byte K fragment reads and the transposing V reads each hit distinct bank
-// groups.  Inside each MFMA run the LDS fragments are read kAhead MFMAs ahead
-// of use (pinned with scheduling barriers) and the wave raises its issue
-// priority, so the other wave on the SIMD fills the VALU (softmax) while this
-// one feeds the matrix core.  The reference max is raised only when a row's max grows past it by
-// more than 2^8 (exact: O and l share the reference), so the O rescale is rare.
-// The row sum l adds the unrounded f32 probabilities, so the LSE stays exact to
-// f32 rounding whatever chunk order the tiles are visited in.
+// K ring and a V ring of four stages each, tile j+3's K and tile j+2's V issued
+// at the start of softmax phase j.  Staged rows are not padded: 16-byte chunks
+// are XOR-swizzled per row so that the 16-byte K fragment reads and the
+// transposing V reads each hit distinct bank groups.  Inside each MFMA run the
+// LDS fragments are read kAhead MFMAs ahead of use (pinned with scheduling
+// barriers).
+//
+// Q is multiplied by scale * log2(e) and rounded to bf16 once per query tile,
+// and each K.Q^T accumulator starts from minus the row's reference max m, so
+// the MFMA delivers the base-2 score minus the reference and a probability is
+// one exp2: the softmax costs 32 exp2, 32 adds and 16 packs per 64-key tile and
+// wave.  The reference is raised only when a row's max grows past it by more
+// than 2^8 (exact: O and l share the reference), so the O rescale is rare.  The
+// row sum l adds the unrounded f32 probabilities.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace chain {
@@ -81,6 +91,7 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 
 
 template <int D, int NW, int WH>
 __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
+  static_assert(NW == 8, "two groups of four waves: one wave of each group per SIMD");
   constexpr int WQ = NW / WH;               // 32-row query blocks per head
   constexpr int ROWS = 32 * WQ;             // query positions per tile
   constexpr int KS = D / 16;                // k-steps of K.Q^T
@@ -89,16 +100,18 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int RPL = 64 / CPR;             // rows per 1 KB wave load
   constexpr int TB = BN * RB;               // bytes of one staged K or V tile
-  constexpr int SB = 2 * TB;                // a stage: the K tile, then the V tile
-  constexpr int NST = 4;                    // stages in the ring
+  constexpr int NST = 4;                    // stages in each of the K and V rings
   constexpr int LPW = BN / RPL / NW;        // 1 KB loads per wave, operand and tile
-  constexpr int LT = 2 * LPW;               // per tile
   static_assert(LPW * RPL * NW == BN, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char lds[NST * SB];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * NST * TB];
+  char *const kring = lds;
+  char *const vring = lds + NST * TB;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
+  // Waves w and w+4 share a SIMD; group 0 is waves 0-3, group 1 waves 4-7.
+  const int grp = wave >> 2;
 
   // ---- work item: (batch, head group, pair of query tiles t and T-1-t)
   const int group = p.Hq / p.Hkv;
@@ -140,7 +153,13 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     kch[q] = (lane % CPR) ^ kswz(lrow[q]);
     vch[q] = (lane % CPR) ^ vswz(lrow[q]);
   }
-  // Per-lane byte offsets of the MFMA fragments within a stage.
+  int klo[LPW], vlo[LPW];   // per-lane byte offsets of a whole tile's loads from its first key
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    klo[q] = lrow[q] * kss2 + 16 * kch[q];
+    vlo[q] = lrow[q] * vss2 + 16 * vch[q];
+  }
+  // Per-lane byte offsets of the MFMA fragments within a K or a V stage.
   int koff[KS], voff[DB];
   {
     const int xk = kswz(l32);
@@ -150,7 +169,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     const int ylane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int xv = D == 128 ? (trow & 3) : ((trow >> 1) & 1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) voff[db] = TB + trow * RB + ((4 * (db ^ xv) + ylane) << 4) + 8 * (lane & 1);
+    for (int db = 0; db < DB; ++db) voff[db] = trow * RB + ((4 * (db ^ xv) + ylane) << 4) + 8 * (lane & 1);
   }
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -172,209 +191,273 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     {
       const __bf16 *qrow = (const __bf16 *)p.q + b * p.q_sb + head * p.q_sh +
                            (int64_t)min(my_row, p.Sq - 1) * p.q_ss + 8 * h2;
+      // Q times scale * log2(e), rounded to bf16: the products then come out of
+      // the MFMA in base-2 units.
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = *(const bf16x8 *)(qrow + ks * 16);
-        if (!row_ok) qf[ks] = bf16x8{};
+        const bf16x8 raw = *(const bf16x8 *)(qrow + ks * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = row_ok ? (__bf16)((float)raw[e] * c) : (__bf16)0.f;
       }
     }
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    // m: the reference max (base 2) of this lane's row, -inf until set; the K.Q^T
+    // accumulators start from -mu, mu = m (0 while m is -inf), so they hold the
+    // scores minus the reference and the fast path's probability is one exp2.
+    float m = -INFINITY, l = 0.f, mu = 0.f;
+    f32x16 mref = f32x16{};   // -mu in every element
+    bool ref_ready = false;   // every lane of the wave holds a finite reference max
+    f32x16 s[2];
+    bf16x8 pk[2][2];
 
-    // ---- tile iterator (uniform over the workgroup)
-    auto range_live = [&](int ri) {
-      return p.kr.end[ri] > p.kr.beg[ri] && (!p.causal || p.kr.beg[ri] + p.kr.pos_off[ri] <= wg_qmax);
+    // ---- tile iterators (uniform over the workgroup).  Tiles of BN keys are
+    // cut inside each key range, up to the last key position this tile's
+    // queries can see (stop); n counts them.  Stepping within a range is one
+    // add and one compare; the range switch is rare.
+    struct It { int ri, k0, stop, kend, off; };   // ri == p.kr.n: past the last tile
+    auto range_stop = [&](int r) {
+      return p.causal ? min(p.kr.end[r], wg_qmax - p.kr.pos_off[r] + 1) : p.kr.end[r];
     };
-    auto advance = [&](int &ri, int &k0) -> bool {
-      k0 += BN;
-      if (k0 < p.kr.end[ri] && (!p.causal || k0 + p.kr.pos_off[ri] <= wg_qmax)) return true;
-      for (++ri; ri < p.kr.n; ++ri)
-        if (range_live(ri)) { k0 = p.kr.beg[ri]; return true; }
-      return false;
+    auto seek = [&](int r) -> It {   // first tile of the first live range at or after r
+      for (; r < p.kr.n; ++r) {
+        const int st = range_stop(r);
+        if (st > p.kr.beg[r]) return It{r, p.kr.beg[r], st, p.kr.end[r], p.kr.pos_off[r]};
+      }
+      return It{p.kr.n, 0, 0, 0, 0};
     };
-    struct Tl { int ri, k0, kend, off; bool valid; };   // range end and position offset cached
-    auto first_tile = [&]() -> Tl {
-      for (int r = 0; r < p.kr.n; ++r)
-        if (range_live(r)) return Tl{r, p.kr.beg[r], p.kr.end[r], p.kr.pos_off[r], true};
-      return Tl{0, 0, 0, 0, false};
+    auto step = [&](It &x) {
+      x.k0 += BN;
+      if (x.k0 >= x.stop) x = seek(x.ri + 1);
     };
-    auto next_tile = [&](Tl x) -> Tl {
-      if (!x.valid) return x;
-      int r = x.ri, k = x.k0;
-      return advance(r, k) ? Tl{r, k, p.kr.end[r], p.kr.pos_off[r], true} : Tl{0, 0, 0, 0, false};
+    auto valid = [&](const It &x) { return x.ri < p.kr.n; };
+    int n = 0;
+    for (int r = 0; r < p.kr.n; ++r) {
+      const int st = range_stop(r);
+      if (st > p.kr.beg[r]) n += (st - p.kr.beg[r] + BN - 1) / BN;
+    }
+    // What this wave does with a tile: skip it, take it whole, or mask it.
+    auto tile_class = [&](const It &x) -> int {
+      if (!valid(x) || !wave_rows) return TILE_SKIP;
+      const int nvalid = min(BN, x.kend - x.k0);
+      return classify_tile(p.causal, w_qmin, w_qmax, x.k0 + x.off, x.k0 + nvalid - 1 + x.off, nvalid < BN);
     };
-    // Direct-to-LDS loads of one tile into stage st: each wave-level load puts
-    // 64 lanes x 16 bytes (RPL key rows) into LDS.  Keys past the range end
-    // read its last key; zero_tail clears them once they have landed.
-    auto issue = [&](const Tl &x, int st) {
-      char *sb = lds + st * SB;
-      const int kend = x.kend;
-#pragma unroll
-      for (int q = 0; q < LPW; ++q) {
-        const uint32_t key = (uint32_t)min(x.k0 + lrow[q], kend - 1);
-        char *dst = sb + (wave * LPW + q) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)dst, 16,
-                                                 key * kss2 + 16 * kch[q], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void *)(dst + TB), 16,
-                                                 key * vss2 + 16 * vch[q], 0, 0, 0);
+    // Direct-to-LDS loads of one operand of one tile into a ring stage: each
+    // wave-level load puts 64 lanes x 16 bytes (RPL key rows) into LDS.  A
+    // whole tile takes its key offset in the scalar offset of the load; in a
+    // tile cut short by its range end, keys past the end read its last key
+    // (their scores are masked, their V rows cleared).
+    auto issue_one = [&](const __amdgpu_buffer_rsrc_t &rs, uint32_t ss2, const int *ch, const int *lo,
+                         const It &x, char *stage, int q) {
+      auto *dst = (__attribute__((address_space(3))) void *)(stage + (wave * LPW + q) * 1024);
+      if (x.k0 + BN <= x.kend) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, lo[q], (uint32_t)x.k0 * ss2, 0, 0);
+      } else {
+        const uint32_t key = (uint32_t)min(x.k0 + lrow[q], x.kend - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, key * ss2 + 16 * ch[q], 0, 0, 0);
       }
     };
-    auto zero_tail = [&](const Tl &x, int st) {
-      const int kend = x.kend;
-      char *sb = lds + st * SB + lane * 16;
-      const u32x4 z = {0u, 0u, 0u, 0u};
+    auto issue = [&](const __amdgpu_buffer_rsrc_t &rs, uint32_t ss2, const int *ch, const int *lo,
+                     const It &x, char *stage) {
 #pragma unroll
-      for (int q = 0; q < LPW; ++q)
-        if (x.k0 + lrow[q] >= kend) {
-          *(u32x4 *)(sb + (wave * LPW + q) * 1024) = z;
-          *(u32x4 *)(sb + TB + (wave * LPW + q) * 1024) = z;
-        }
+      for (int q = 0; q < LPW; ++q) issue_one(rs, ss2, ch, lo, x, stage, q);
     };
-    auto compute = [&](const Tl &x, const int st) {
-      const int k0 = x.k0;
-      // ---- compute on the staged tile
-      const int off = x.off;
-      const int nvalid = min(BN, x.kend - k0);
-      const int cls = classify_tile(p.causal, w_qmin, w_qmax, k0 + off, k0 + nvalid - 1 + off, nvalid < BN);
-      if (wave_rows && cls != TILE_SKIP) {
-        const char *sb = lds + st * SB;
-        f32x16 s[2] = {f32x16{}, f32x16{}};
-        __builtin_amdgcn_s_setprio(1);
-        {
-          constexpr int N = 2 * KS;
-          auto addr = [&](int i) { return sb + koff[i >> 1] + (i & 1) * 32 * RB; };
-          bf16x8 kf[kAhead];
+    // V rows past a range end are cleared once this wave's own loads of them
+    // have landed, so that a masked key multiplies zeros whatever the input holds.
+    auto zero_v_tail = [&](const It &x, char *stage) {
+      if (valid(x) && x.k0 + BN > x.kend) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int i = 0; i < kAhead; ++i) kf[i] = *(const bf16x8 *)addr(i);
+        for (int q = 0; q < LPW; ++q)
+          if (x.k0 + lrow[q] >= x.kend) *(u32x4 *)(stage + (wave * LPW + q) * 1024 + lane * 16) = z;
+        wait_lgkmcnt0();
+      }
+    };
+    // MFMA phase: NQ products of S^T = K.Q^T on a K stage, then NP products
+    // of O^T += V^T.P^T on a V stage (the previous tile's P).  LDS fragments
+    // are read kAhead MFMAs ahead of use, across the boundary of the two runs.
+    auto mfma_run = [&](auto nq_c, auto np_c, const char *ks, const char *vs, auto hook) {
+      constexpr int NQ = decltype(nq_c)::value, NP = decltype(np_c)::value, N = NQ + NP;
+      auto frag = [&](int i) -> bf16x8 {
+        if (i < NQ) return *(const bf16x8 *)(ks + koff[i >> 1] + (i & 1) * 32 * RB);
+        const int k = i - NQ;
+        const __bf16 *a = (const __bf16 *)(vs + voff[k >> 2] + (((k >> 1) & 1) * 32 + 16 * (k & 1)) * RB);
+        const i16x4 lo = ds_read_tr(a), hi = ds_read_tr(a + 8 * D);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 f[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i)
+        if (i < N) f[i] = frag(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < N; ++i) {
-            const bf16x8 a = kf[i % kAhead];
-            if (i + kAhead < N) kf[i % kAhead] = *(const bf16x8 *)addr(i + kAhead);
-            s[i & 1] = mfma32(a, qf[i >> 1], s[i & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+      for (int i = 0; i < N; ++i) {
+        const bf16x8 a = f[i % kAhead];
+        if (i + kAhead < N) f[i % kAhead] = frag(i + kAhead);
+        if (i < NQ) {
+          s[i & 1] = mfma32(a, qf[i >> 1], i < 2 ? mref : s[i & 1]);
+        } else {
+          const int k = i - NQ;
+          acc[k >> 2] = mfma32(a, pk[(k >> 1) & 1][k & 1], acc[k >> 2]);
         }
-        __builtin_amdgcn_s_setprio(0);
-        if (cls == TILE_DIAG) {
-          // key of register r in lane half h2 is kb*32 + 8*(r/4) + 4*h2 + r%4: compare
-          // its compile-time part with per-lane limits (branch-free selects)
-          const int lim_c = p.causal ? my_qpos - k0 - off - 4 * h2 : BN;
-          const int lim = min(nvalid - 1 - 4 * h2, lim_c);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kr = kb * 32 + 8 * (r >> 2) + (r & 3);
-              s[kb][r] = kr <= lim ? s[kb][r] : -INFINITY;
-            }
-        }
-        // Fast path: probabilities against the current reference.  The row max
-        // only decides whether the reference must rise (a term above 2^kTau); a
-        // lane sum of at most 2^kTau proves no term is, so the max is computed
-        // (and the rule below applied) only when some lane sum exceeds it, or
-        // before the first reference exists.
-        float rs = 0.f;
-        bf16x8 pk[2][2];
-        bool slow = __any(m == -INFINITY);
-        if (!slow) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m));
-              rs += e;
-              pk[kb][r >> 3][r & 7] = (__bf16)e;
-            }
-          slow = __any(!(rs <= kLaneSumMax));
-        }
-        if (slow) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-          // the reference max is raised only when the row max exceeds it by more
-          // than 2^kTau (exact: O and l share the reference); the O rescale is rare
-          const float tmax = pair_max(mx) * c;
-          if (__any(tmax > m + kTau)) {
-            const float m_new = fmaxf(m, tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
-            m = m_new;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-          }
-          const float m_use = m == -INFINITY ? 0.f : m;
-          rs = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
-              rs += e;
-              pk[kb][r >> 3][r & 7] = (__bf16)e;
-            }
-        }
-        l += rs;
-        // O^T += V^T . P^T
-        __builtin_amdgcn_s_setprio(1);
-        {
-          constexpr int N = 4 * DB;
-          auto addr = [&](int i) {
-            const int db = i >> 2, kb = (i >> 1) & 1, hh = i & 1;
-            return (const __bf16 *)(sb + voff[db] + (kb * 32 + 16 * hh) * RB);
-          };
-          i16x4 vlo[kAhead], vhi[kAhead];
-#pragma unroll
-          for (int i = 0; i < kAhead; ++i) {
-            vlo[i] = ds_read_tr(addr(i));
-            vhi[i] = ds_read_tr(addr(i) + 8 * D);
-          }
-#pragma unroll
-          for (int i = 0; i < N; ++i) {
-            const i16x8 a16 = __builtin_shufflevector(vlo[i % kAhead], vhi[i % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
-            if (i + kAhead < N) {
-              vlo[i % kAhead] = ds_read_tr(addr(i + kAhead));
-              vhi[i % kAhead] = ds_read_tr(addr(i + kAhead) + 8 * D);
-            }
-            acc[i >> 2] = mfma32(__builtin_bit_cast(bf16x8, a16), pk[(i >> 1) & 1][i & 1], acc[i >> 2]);
+        hook(i);
         __builtin_amdgcn_sched_barrier(0);
-          }
-        }
       }
-      __builtin_amdgcn_s_setprio(0);
+    };
+    using QK = std::integral_constant<int, 2 * KS>;
+    using PV = std::integral_constant<int, 4 * DB>;
+    using NONE = std::integral_constant<int, 0>;
+    // Softmax phase on the scores of one tile: probabilities P (bf16, the B
+    // operand of the next P.V run), the row sum l and the lazily raised
+    // reference max m.
+    auto softmax = [&](const It &x, int cls) {
+      if (cls == TILE_DIAG) {
+        // key of register r in lane half h2 is kb*32 + 8*(r/4) + 4*h2 + r%4: compare
+        // its compile-time part with per-lane limits (branch-free selects)
+        const int nvalid = min(BN, x.kend - x.k0);
+        const int lim_c = p.causal ? my_qpos - x.k0 - x.off - 4 * h2 : BN;
+        const int lim = min(nvalid - 1 - 4 * h2, lim_c);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr = kb * 32 + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = kr <= lim ? s[kb][r] : -INFINITY;
+          }
+      }
+      // Fast path: probabilities against the current reference.  The row max
+      // only decides whether the reference must rise (a term above 2^kTau); a
+      // lane sum of at most 2^kTau proves no term is, so the max is computed
+      // (and the rule below applied) only when some lane sum exceeds it, or
+      // before the first reference exists.
+      float rs = 0.f;
+      bool slow = !ref_ready;
+      if (!slow) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(s[kb][r]);
+            rs += e;
+            pk[kb][r >> 3][r & 7] = (__bf16)e;
+          }
+        slow = __any(!(rs <= kLaneSumMax));
+      }
+      if (slow) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        // the reference max is raised only when the row max exceeds it by more
+        // than 2^kTau (exact: O and l share the reference); the O rescale is rare
+        const float tmax = pair_max(mx) + mu;
+        if (__any(tmax > m + kTau)) {
+          const float m_new = fmaxf(m, tmax);
+          const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+          m = m_new;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        }
+        // the scores hold s - mu; shift them to the (possibly new) reference
+        const float mu_new = m == -INFINITY ? 0.f : m;
+        const float d = mu_new - mu;
+        mu = mu_new;
+        mref = -mu;
+        rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(s[kb][r] - d);
+            rs += e;
+            pk[kb][r >> 3][r & 7] = (__bf16)e;
+          }
+        ref_ready = !__any(m == -INFINITY);
+      }
+      l += rs;
+    };
+    auto barrier = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Ring of NST stages (tile j in stage j % NST), fetched three tiles ahead.
-    // Past the last tile the free stage is refilled with the current tile, so
-    // every step has the same number of loads in flight.  Stage j+3 reuses the
-    // buffer of tile j-1, whose reads finished before the previous barrier.
-    Tl w0 = first_tile(), w1 = next_tile(w0), w2 = next_tile(w1), w3 = next_tile(w2);
-    if (w0.valid) {
-      issue(w0, 0);
-      issue(w1.valid ? w1 : w0, 1);
-      issue(w2.valid ? w2 : w0, 2);
-      wait_vmcnt<2 * LT>();
-      if (w0.k0 + BN > w0.kend) zero_tail(w0, 0);
-    }
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    int j = 0;
-    while (w0.valid) {
-      issue(w3.valid ? w3 : w0, (j + 3) % NST);
-      compute(w0, j % NST);
-      wait_vmcnt<2 * LT>();   // this wave's part of tile j+1 has landed
-      if (w1.valid && w1.k0 + BN > w1.kend) zero_tail(w1, (j + 1) % NST);
-      wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();
-      w0 = w1;
-      w1 = w2;
-      w2 = w3;
-      w3 = next_tile(w3);
-      ++j;
+    // ---- ping-pong over the tiles.  Each wave runs C_0 S_0 C_1 S_1 ... C_n, with
+    // C_j = [K.Q^T of tile j, P.V of tile j-1] on the matrix core and S_j = the
+    // softmax of tile j on the vector ALU; group 1 runs one phase behind group 0,
+    // and every phase ends at a workgroup barrier.  So on each SIMD one wave's
+    // MFMA run meets the other wave's softmax.  In phase ph group 0 runs step
+    // ph and group 1 step ph-1 of that sequence (C_j is step 2j, S_j step 2j+1).
+    //
+    // Tile j's K sits in K stage j%4 and is read in phases 2j and 2j+1; its V
+    // sits in V stage j%4 and is read in phases 2j+2 and 2j+3.  S_j issues K of
+    // tile j+3 and V of tile j+2 (phase 2j+1 or 2j+2), whose stages were last
+    // read in phase 2j-1.  Past the last tile the free stages are refilled with
+    // tile j, so every step has the same loads in flight.  Per wave the load
+    // groups (LPW loads each) are issued in the order K0 V0 K1 V1 K2 | K3 V2 |
+    // K4 V3 | ..., and a tile's K and V must have landed before the barrier
+    // ahead of the phase that first reads them: group 0 waits at the end of
+    // each S step for all but its last 4 groups, group 1 at the end of each C
+    // step for all but its last 2.
+    if (n > 0) {
+      // cur: tile j (K.Q^T, softmax); itv: tile j+2 and itk: tile j+3, whose V
+      // and K are loaded in S_j.  Past the last tile the loads repeat the first
+      // tile into the free stages, so every step has the same loads in flight.
+      const It first = seek(0);
+      It cur = first, itv = first, itk = first;
+      step(itv);
+      issue(krs, kss2, kch, klo, cur, kring);
+      issue(vrs, vss2, vch, vlo, cur, vring);
+      issue(krs, kss2, kch, klo, valid(itv) ? itv : first, kring + TB);
+      issue(vrs, vss2, vch, vlo, valid(itv) ? itv : first, vring + TB);
+      step(itv);
+      itk = itv;
+      issue(krs, kss2, kch, klo, valid(itk) ? itk : first, kring + 2 * TB);
+      step(itk);
+      wait_vmcnt<4 * LPW>();   // K of tile 0 has landed
+      barrier();
+      int cls = tile_class(cur);
+      bool prev_live = false;
+      // C_j: the K.Q^T run of tile j (in K stage j%4), then the P.V run of tile
+      // j-1 (in V stage (j-1)%4).
+      auto mfma_step = [&](int j) {
+        const char *ks = kring + (j % NST) * TB;
+        const char *vs = vring + ((j + NST - 1) % NST) * TB;
+        __builtin_amdgcn_s_setprio(1);
+        if (cls != TILE_SKIP) mfma_run(QK{}, NONE{}, ks, vs, [](int) {});
+        if (prev_live) mfma_run(NONE{}, PV{}, ks, vs, [](int) {});
+        __builtin_amdgcn_s_setprio(0);
+        if (grp == 1) {
+          wait_vmcnt<2 * LPW>();
+          zero_v_tail(cur, vring + (j % NST) * TB);
+        }
+      };
+      if (grp == 1) barrier();   // group 1 runs one phase behind
+      for (int j = 0; j < n; ++j) {
+        mfma_step(j);
+        barrier();
+        // S_j: this wave's part of tile j+3's K and tile j+2's V goes out first,
+        // so that the loads are in flight during the softmax
+        issue(krs, kss2, kch, klo, valid(itk) ? itk : first, kring + ((j + 3) % NST) * TB);
+        issue(vrs, vss2, vch, vlo, valid(itv) ? itv : first, vring + ((j + 2) % NST) * TB);
+        if (cls != TILE_SKIP) softmax(cur, cls);
+        if (grp == 0) {
+          wait_vmcnt<4 * LPW>();
+          zero_v_tail(cur, vring + (j % NST) * TB);
+        }
+        prev_live = cls != TILE_SKIP;
+        step(cur);
+        step(itv);
+        step(itk);
+        cls = tile_class(cur);
+        barrier();
+      }
+      mfma_step(n);              // P.V of the last tile
+      barrier();
+      if (grp == 0) barrier();   // group 0 waits out group 1's last phase
     }
     wait_vmcnt<0>();   // no load into LDS may outlive the pass
     __builtin_amdgcn_s_barrier();

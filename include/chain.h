@@ -138,7 +138,10 @@ const char *chain_last_error(void);
  *            of S into 2*n_chunks equal pieces (TSP article, zigzag partition);
  *            zero: chunk s is the s-th of n_chunks contiguous ranges
  * The result does not depend on n_chunks/zigzag beyond floating-point
- * rounding.  D must be 64 or 128, and for bf16 the key (and the value) rows
+ * rounding.  bf16 inputs: products are bf16 MFMAs with f32 accumulation; Q
+ * times scale * log2(e) and the probabilities are rounded to bf16 as MFMA
+ * operands; f32 inputs are computed in f32 throughout.  D must be 64 or 128,
+ * and for bf16 the key (and the value) rows
  * of one head must span less than 2^31 bytes, i.e. ((S - 1) * stride + D) * 2
  * < 2^31 (CHAIN_ERR_UNSUPPORTED otherwise).
  */
