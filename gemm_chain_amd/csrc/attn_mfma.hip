@@ -132,11 +132,10 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   const float c = p.scale_log2;
   // Buffer descriptors over this head's K and V rows (byte offsets fit 32 bits:
   // the host checks that a head's rows span less than 2^31 bytes).
+  // Byte offsets of key rows from these bases fit 32 bits: the host checks
+  // that a head's rows span less than 2^31 bytes.
   const uint32_t kss2 = (uint32_t)p.k_ss * 2u, vss2 = (uint32_t)p.v_ss * 2u;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)kbase, 0, (int)((uint32_t)(p.Sk - 1) * kss2 + 2 * D), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)vbase, 0, (int)((uint32_t)(p.Sk - 1) * vss2 + 2 * D), 0x00020000);
+  const char *kb8 = (const char *)kbase, *vb8 = (const char *)vbase;
 
   // Rows of a staged tile are not padded: 16-byte chunk c of key row r sits at
   // chunk c ^ kswz(r) in K and c ^ vswz(r) in V.  kswz spreads the 16-byte
@@ -244,24 +243,18 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       return classify_tile(p.causal, w_qmin, w_qmax, x.k0 + x.off, x.k0 + nvalid - 1 + x.off, nvalid < BN);
     };
     // Direct-to-LDS loads of one operand of one tile into a ring stage: each
-    // wave-level load puts 64 lanes x 16 bytes (RPL key rows) into LDS.  A
-    // whole tile takes its key offset in the scalar offset of the load; in a
-    // tile cut short by its range end, keys past the end read its last key
-    // (their scores are masked, their V rows cleared).
-    auto issue_one = [&](const __amdgpu_buffer_rsrc_t &rs, uint32_t ss2, const int *ch, const int *lo,
-                         const It &x, char *stage, int q) {
-      auto *dst = (__attribute__((address_space(3))) void *)(stage + (wave * LPW + q) * 1024);
-      if (x.k0 + BN <= x.kend) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, lo[q], (uint32_t)x.k0 * ss2, 0, 0);
-      } else {
-        const uint32_t key = (uint32_t)min(x.k0 + lrow[q], x.kend - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, key * ss2 + 16 * ch[q], 0, 0, 0);
-      }
-    };
-    auto issue = [&](const __amdgpu_buffer_rsrc_t &rs, uint32_t ss2, const int *ch, const int *lo,
-                     const It &x, char *stage) {
+    // wave-level load puts 64 lanes x 16 bytes (RPL key rows) into LDS.  The
+    // buffer descriptor starts at the tile's first key row and ends at its
+    // range end, so the same branch-free loads serve whole tiles and tiles cut
+    // short: keys past the range end are out of the buffer and read as zero
+    // (their scores are masked, their V rows cleared as well).
+    auto issue = [&](const char *base, uint32_t ss2, const int *lo, const It &x, char *stage) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(base + (uint32_t)x.k0 * ss2), 0, (int)((uint32_t)(x.kend - x.k0 - 1) * ss2 + 2 * D), 0x00020000);
 #pragma unroll
-      for (int q = 0; q < LPW; ++q) issue_one(rs, ss2, ch, lo, x, stage, q);
+      for (int q = 0; q < LPW; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(stage + (wave * LPW + q) * 1024),
+                                                 16, lo[q], 0, 0, 0);
     };
     // V rows past a range end are cleared once this wave's own loads of them
     // have landed, so that a masked key multiplies zeros whatever the input holds.
@@ -409,13 +402,13 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       const It first = seek(0);
       It cur = first, itv = first, itk = first;
       step(itv);
-      issue(krs, kss2, kch, klo, cur, kring);
-      issue(vrs, vss2, vch, vlo, cur, vring);
-      issue(krs, kss2, kch, klo, valid(itv) ? itv : first, kring + TB);
-      issue(vrs, vss2, vch, vlo, valid(itv) ? itv : first, vring + TB);
+      issue(kb8, kss2, klo, cur, kring);
+      issue(vb8, vss2, vlo, cur, vring);
+      issue(kb8, kss2, klo, valid(itv) ? itv : first, kring + TB);
+      issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + TB);
       step(itv);
       itk = itv;
-      issue(krs, kss2, kch, klo, valid(itk) ? itk : first, kring + 2 * TB);
+      issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + 2 * TB);
       step(itk);
       wait_vmcnt<4 * LPW>();   // K of tile 0 has landed
       barrier();
@@ -441,8 +434,8 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         barrier();
         // S_j: this wave's part of tile j+3's K and tile j+2's V goes out first,
         // so that the loads are in flight during the softmax
-        issue(krs, kss2, kch, klo, valid(itk) ? itk : first, kring + ((j + 3) % NST) * TB);
-        issue(vrs, vss2, vch, vlo, valid(itv) ? itv : first, vring + ((j + 2) % NST) * TB);
+        issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + ((j + 3) % NST) * TB);
+        issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + ((j + 2) % NST) * TB);
         if (cls != TILE_SKIP) softmax(cur, cls);
         if (grp == 0) {
           wait_vmcnt<4 * LPW>();
