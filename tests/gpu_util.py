@@ -45,3 +45,21 @@ def sample_rows(S, n, seed, extra=()):
     rows.update(r for r in (0, 1, 2, 3, S - 1, S - 2) if 0 <= r < S)
     rows.update(int(r) for r in extra if 0 <= r < S)
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def host_threads():
+    """Worker threads for host-side reference work: the CPU share of the box, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_threaded(jobs):
+    """Run callables on host threads, one BLAS thread each, and return their results in
+    order.  Threads, not processes: the test process holds the GPU, and numpy's BLAS
+    calls and large ufuncs release the GIL."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(host_threads()) as ex:
+            return list(ex.map(lambda f: f(), jobs))
