@@ -1,8 +1,16 @@
 """GPU parity of chain_linear_attn_fwd (causal linear attention with a carried
 key/value state) against the float64 oracle.
 
-Tolerance, element by element, from where the kernels round (Q, K, V and S_in
-are the same values on both sides).  The output pass takes the rows in pieces
+Tolerance, element by element, independent of how the kernels are organised:
+the componentwise bound of the definition evaluated in absolute values,
+  |O_gpu - O_exact|_ie <= GAMMA * (sum_{j<=i} (|q_i| . |k_j|) |v_je| + sum_d |q_id| |S_in,de|),
+with GAMMA = 2^-6, which covers up to two bf16 roundings (unit roundoff 2^-9) of
+any score, state or product on the way to an output element, on top of f32
+accumulation; the state path is covered because |q_i S| <= sum_j (|q_i|.|k_j|)|v_j|
+for S = sum_j k_j^T v_j.  It is asserted for every case, at every size.
+
+For diagnosis only, the tests also print the error against a tighter bound
+derived from where these kernels round.  The output pass takes the rows in pieces
 (64 rows at D = 128, 128 at D = 64).  Inside a piece the scores q_i . k_j are
 rounded to bf16 as an MFMA operand; the state before the piece is rounded to
 bf16 once, from its f32 value; everything else accumulates in f32.  So, with j
@@ -27,6 +35,24 @@ pytestmark = pytest.mark.gpu
 
 EPS = 2.0 ** -8
 ACC = 2.0 ** -14
+GAMMA = 2.0 ** -6
+
+
+def _abs_bound(q, k, v, s_in, rows=None):
+    """GAMMA times the definition evaluated in absolute values, at the given rows."""
+    B, Hq, S, D = q.shape
+    group = Hq // k.shape[1]
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    out = np.zeros((B, Hq, len(rows), D))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            qa = np.abs(q[b, h, rows])
+            sc = (qa @ np.abs(k[b, g]).T) * (np.arange(S)[None, :] <= rows[:, None])
+            out[b, h] = sc @ np.abs(v[b, g])
+            if s_in is not None:
+                out[b, h] += qa @ np.abs(s_in[b, g])
+    return GAMMA * out
 
 
 def piece_rows(D):
@@ -59,16 +85,19 @@ def _bound(q, k, v, s_in):
     return bound
 
 
-def _check(name, got, ref, bound):
+def _check(name, got, ref, bound, derived=None):
+    """bound: the implementation-independent elementwise bound (asserted);
+    derived: the bound from these kernels' rounding points (printed only)."""
     got = np.asarray(got, dtype=np.float64)
     assert got.shape == ref.shape
     assert np.isfinite(got).all(), f"{name}: non-finite output"
     err = np.abs(got - ref)
     floor = 1e-6 * max(1.0, float(np.abs(ref).max()))
     rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
+    diag = "" if derived is None else f"  err/derived {float((err / (derived + floor)).max()):.3f}"
     print(f"{name}: max-abs {err.max():.3e}  max|ref| {np.abs(ref).max():.3e}  "
-          f"err/bound {float((err / (bound + floor)).max()):.3f}  rel-fro {rel:.2e}")
-    assert np.all(err <= bound + floor), f"{name}: error above the derived bound"
+          f"err/bound {float((err / (bound + floor)).max()):.3f}{diag}  rel-fro {rel:.2e}")
+    assert np.all(err <= bound + floor), f"{name}: error above the elementwise bound"
     assert rel <= 2.0 ** -7, f"{name}: relative error {rel:.2e}"
 
 
@@ -96,7 +125,7 @@ def test_linear_attention_small_full_compare(B, Hq, Hkv, S, D, with_state):
     torch.cuda.synchronize()
     sn = f64(s_in) if with_state else None
     ro, rs = oracle.linear_attention(f64(q), f64(k), f64(v), sn)
-    _check("O", f64(o), ro, _bound(f64(q), f64(k), f64(v), sn))
+    _check("O", f64(o), ro, _abs_bound(f64(q), f64(k), f64(v), sn), _bound(f64(q), f64(k), f64(v), sn))
     # the state: f32 sums of exact bf16 products
     kv_abs = np.einsum("bgjd,bgje->bgde", np.abs(f64(k)), np.abs(f64(v)))
     serr = np.abs(f64(so) - rs)
@@ -120,7 +149,9 @@ def test_linear_attention_state_passing_between_shares():
     # the state is rounded, so it is held to the oracle bound like the whole
     assert torch.equal(o1, whole[:, :, :cut])
     ro, rs = oracle.linear_attention(f64(q), f64(k), f64(v), f64(s_in))
-    _check("O second share", f64(o2), ro[:, :, cut:], _bound(f64(q), f64(k), f64(v), f64(s_in))[:, :, cut:])
+    _check("O second share", f64(o2), ro[:, :, cut:],
+           _abs_bound(f64(q), f64(k), f64(v), f64(s_in))[:, :, cut:],
+           _bound(f64(q), f64(k), f64(v), f64(s_in))[:, :, cut:])
     assert np.max(np.abs(f64(s2) - rs)) <= 1e-3 * np.abs(rs).max()
 
 
@@ -150,10 +181,8 @@ def test_linear_attention_full_size_sampled_rows():
     qn, kn, vn, sn = f64(q[:, heads]), f64(k[:, heads]), f64(v[:, heads]), f64(s_in[:, heads])
     ref = oracle.linear_attention_rows(qn, kn, vn, rows, sn)
     got = f64(o[:, heads].cpu())[:, :, rows]
-    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    print(f"sampled rows: rel-fro {rel:.2e}")
     assert np.isfinite(f64(o)).all()
-    assert rel <= 2.0 ** -7
+    _check("O sampled rows", got, ref, _abs_bound(qn, kn, vn, sn, rows))
     rs = sn + np.einsum("bgjd,bgje->bgde", kn, vn)
     srel = np.abs(f64(so[:, heads].cpu()) - rs).max() / np.abs(rs).max()
     print(f"state: max-abs/max {srel:.2e}")
