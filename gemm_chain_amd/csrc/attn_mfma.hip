@@ -415,40 +415,65 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       int cls = tile_class(cur);
       bool prev_live = false;
       // C_j: the K.Q^T run of tile j (in K stage j%4), then the P.V run of tile
-      // j-1 (in V stage (j-1)%4).
-      auto mfma_step = [&](int j) {
-        const char *ks = kring + (j % NST) * TB;
-        const char *vs = vring + ((j + NST - 1) % NST) * TB;
+      // j-1 (in V stage (j-1)%4).  The loop is unrolled over the four ring
+      // stages, so that every LDS address is a per-lane offset plus an immediate.
+      auto mfma_step = [&](auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        const char *ks = kring + ST * TB;
+        const char *vs = vring + ((ST + NST - 1) % NST) * TB;
         __builtin_amdgcn_s_setprio(1);
         if (cls != TILE_SKIP) mfma_run(QK{}, NONE{}, ks, vs, [](int) {});
         if (prev_live) mfma_run(NONE{}, PV{}, ks, vs, [](int) {});
         __builtin_amdgcn_s_setprio(0);
         if (grp == 1) {
           wait_vmcnt<2 * LPW>();
-          zero_v_tail(cur, vring + (j % NST) * TB);
+          zero_v_tail(cur, vring + ST * TB);
         }
       };
-      if (grp == 1) barrier();   // group 1 runs one phase behind
-      for (int j = 0; j < n; ++j) {
-        mfma_step(j);
-        barrier();
-        // S_j: this wave's part of tile j+3's K and tile j+2's V goes out first,
-        // so that the loads are in flight during the softmax
-        issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + ((j + 3) % NST) * TB);
-        issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + ((j + 2) % NST) * TB);
+      // S_j: this wave's part of tile j+3's K and tile j+2's V goes out first,
+      // so that the loads are in flight during the softmax
+      auto softmax_step = [&](auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + ((ST + 3) % NST) * TB);
+        issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + ((ST + 2) % NST) * TB);
         if (cls != TILE_SKIP) softmax(cur, cls);
         if (grp == 0) {
           wait_vmcnt<4 * LPW>();
-          zero_v_tail(cur, vring + (j % NST) * TB);
+          zero_v_tail(cur, vring + ST * TB);
         }
         prev_live = cls != TILE_SKIP;
         step(cur);
         step(itv);
         step(itk);
         cls = tile_class(cur);
+      };
+      using St0 = std::integral_constant<int, 0>;
+      using St1 = std::integral_constant<int, 1>;
+      using St2 = std::integral_constant<int, 2>;
+      using St3 = std::integral_constant<int, 3>;
+      static_assert(NST == 4, "the loop is unrolled over four stages");
+      // tiles past the last (up to a multiple of four) are skipped by every wave
+      const int n4 = (n + NST - 1) / NST * NST;
+      if (grp == 1) barrier();   // group 1 runs one phase behind
+      for (int j = 0; j < n4; j += NST) {
+        mfma_step(St0{});
+        barrier();
+        softmax_step(St0{});
+        barrier();
+        mfma_step(St1{});
+        barrier();
+        softmax_step(St1{});
+        barrier();
+        mfma_step(St2{});
+        barrier();
+        softmax_step(St2{});
+        barrier();
+        mfma_step(St3{});
+        barrier();
+        softmax_step(St3{});
         barrier();
       }
-      mfma_step(n);              // P.V of the last tile
+      mfma_step(St0{});          // P.V of the last tile (stage (n4-1) % 4 = 3)
       barrier();
       if (grp == 0) barrier();   // group 0 waits out group 1's last phase
     }
