@@ -31,6 +31,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 HEADLINE = "attn_gqa_bf16_h32kv8_s65536_d128"
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 FLUSH_BYTES = 1 << 30         # written between cold merge calls
+WARM_MS = 100.0               # warm-up of each secondary workload before timing
 
 
 def committed_traffic():
@@ -61,16 +62,23 @@ def attn_flops(B, Hq, Sq, Sk, D, causal=True):
     return f / 2 if causal else f
 
 
-def time_region(torch, fn, steps, warmup, stream, per_step=None, before=None):
+def time_region(torch, fn, steps, warmup, stream, per_step=None, before=None, warmup_ms=0.0):
     """Mean ms per call of fn over `steps` calls, HIP events on `stream`.  If
     per_step is a list, the duration of each call (events between the calls of
     the same timed region) is appended to it.  With `before`, it runs ahead of
     every call outside the timed intervals (each call is then bracketed by its
-    own events and the mean is over those intervals)."""
-    for _ in range(warmup):
+    own events and the mean is over those intervals).  Warm-up: `warmup` calls,
+    continued until at least warmup_ms of wall time have passed (short kernels
+    reach their steady clock only after some milliseconds of work)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < warmup_ms:
         if before:
             before()
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     if before:
         marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -177,7 +185,7 @@ def config_legs(torch, chain, steps, head):
     o = torch.empty_like(qd)
     l = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
     per = []
-    time_region(torch, lambda: chain.attn_fwd(qd, kd, vd, causal=True, out=o, lse=l), steps, 2, stream, per)
+    time_region(torch, lambda: chain.attn_fwd(qd, kd, vd, causal=True, out=o, lse=l), steps, 2, stream, per, warmup_ms=WARM_MS)
     s, tf, fr = rate(attn_flops(w.B, w.Hq, w.S, w.S, w.D), per)
     recs[w.name] = {"ms": s, "gflops": round(attn_flops(w.B, w.Hq, w.S, w.S, w.D) / s["median"] / 1e6, 2),
                     "dtype": "f32"}
@@ -190,7 +198,7 @@ def config_legs(torch, chain, steps, head):
     o = torch.empty_like(qd)
     l = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
     per = []
-    time_region(torch, lambda: chain.attn_fwd(qd, kd, vd, causal=True, out=o, lse=l), steps, 2, stream, per)
+    time_region(torch, lambda: chain.attn_fwd(qd, kd, vd, causal=True, out=o, lse=l), steps, 2, stream, per, warmup_ms=WARM_MS)
     s, tf, fr = rate(attn_flops(w.B, w.Hq, w.S, w.S, w.D), per)
     recs[w.name] = {"ms": s, "tflops": tf, "frac_peak": fr, "dtype": "bf16"}
     checks[w.name] = ("attn", w, (q, k, v), (o.cpu(), l.cpu()), None)
@@ -223,8 +231,8 @@ def config_legs(torch, chain, steps, head):
 
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     per_p, per_m = [], []
-    time_region(torch, partials, steps, 2, stream, per_p)
-    time_region(torch, merge, steps, 2, stream, per_m, before=lambda: flush.fill_(1))
+    time_region(torch, partials, steps, 2, stream, per_p, warmup_ms=WARM_MS)
+    time_region(torch, merge, steps, 2, stream, per_m, before=lambda: flush.fill_(1), warmup_ms=WARM_MS)
     del flush
     n = w.S // (2 * P)
     flops = 4.0 * B * H * D * (2 * P * n * n + n)       # visible pairs of the share: 2 P n^2 + n per head
@@ -247,11 +255,11 @@ def config_legs(torch, chain, steps, head):
     o = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(chain.mlp_workspace_bytes(w.M, w.N), dtype=torch.uint8, device=dev)
     per = []
-    time_region(torch, lambda: chain.mlp_fwd(xd, w1c, w2c, act=w.act, out=o, workspace=ws), steps, 2, stream, per)
+    time_region(torch, lambda: chain.mlp_fwd(xd, w1c, w2c, act=w.act, out=o, workspace=ws), steps, 2, stream, per, warmup_ms=WARM_MS)
     s, tf, fr = rate(4.0 * w.M * w.K * w.N, per)
     w1r, w2r = w1.to(dev), w2.to(dev)
     per_r = []
-    time_region(torch, lambda: chain.mlp_fwd(xd, w1r, w2r, act=w.act, out=o, workspace=ws), steps, 2, stream, per_r)
+    time_region(torch, lambda: chain.mlp_fwd(xd, w1r, w2r, act=w.act, out=o, workspace=ws), steps, 2, stream, per_r, warmup_ms=WARM_MS)
     sr, tfr, frr = rate(4.0 * w.M * w.K * w.N, per_r)
     chain.mlp_fwd(xd, w1c, w2c, act=w.act, out=o, workspace=ws)
     recs[w.name] = {"ms": s, "tflops": tf, "frac_peak": fr, "ms_rowmajor_w": sr, "tflops_rowmajor_w": tfr,
@@ -286,7 +294,7 @@ def secondary(torch, chain, steps, c2):
     bws = torch.empty(chain.attn_bwd_workspace_bytes(w.B, w.Hq, w.S), dtype=torch.uint8, device=dev)
     per = []
     time_region(torch, lambda: chain.attn_bwd(q, k, v, o, l, do, dq=dq, dk=dk, dv=dv, workspace=bws),
-                steps, 2, stream, per)
+                steps, 2, stream, per, warmup_ms=WARM_MS)
     s, tf, fr = rate(2.5 * attn_flops(w.B, w.Hq, w.S, w.S, w.D), per)
     out["attn_bwd_" + w.name] = {"ms": s, "tflops": tf, "frac_peak": fr}
     del do, dq, dk, dv, bws
@@ -300,7 +308,7 @@ def secondary(torch, chain, steps, c2):
     ws = torch.empty(chain.mlp_workspace_bytes(w.M, w.N), dtype=torch.uint8, device=dev)
     per = []
     time_region(torch, lambda: chain.mlp_gated_fwd(x, wg, wu, wd, act=w.act, out=o, workspace=ws),
-                steps, 2, stream, per)
+                steps, 2, stream, per, warmup_ms=WARM_MS)
     s, tf, fr = rate(6.0 * w.M * w.K * w.N, per)
     out[w.name] = {"ms": s, "tflops": tf, "frac_peak": fr}
     del x, wg, wu, wd, o, ws
@@ -315,7 +323,7 @@ def secondary(torch, chain, steps, c2):
     ws = torch.empty(chain.linear_attn_workspace_bytes(w.B, w.Hkv, w.S, w.D), dtype=torch.uint8, device=dev)
     per = []
     time_region(torch, lambda: chain.linear_attn_fwd(q, k, v, s_in=s_in, out=o, s_out=s_out, workspace=ws),
-                steps, 2, stream, per)
+                steps, 2, stream, per, warmup_ms=WARM_MS)
     T = (w.S + 127) // 128
     flops = w.B * w.Hq * (T * 4 * w.D * 128 * 129 / 2 + 2 * w.S * w.D * w.D) + w.B * w.Hkv * 2 * w.S * w.D * w.D
     alg = 3 * q.numel() * 2 + o.numel() * 4 + 2 * s_in.numel() * 4

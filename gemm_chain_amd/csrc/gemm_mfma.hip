@@ -638,10 +638,10 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 
   // Stage kt into ring slot kt % DST; past the last stage, stage 0 again (valid
   // data into a slot nobody reads, so every iteration has the same shape).
-  auto issue = [&](int kt) {
+  auto issue = [&](int kt, auto whole_c) {
     char *sb = lds + (kt & (DST - 1)) * STAGE;
     const int k0 = kt < nk ? kt * DBK : 0;
-    if (k0 + DBK <= p.K) {
+    if (decltype(whole_c)::value || k0 + DBK <= p.K) {
 #pragma unroll
       for (int q = 0; q < LA; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(sb + (wave + 8 * q) * 1024), 16, aoff[q],
@@ -716,9 +716,13 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 
   constexpr int NM = 2 * NBW;   // MFMAs per k-step
   Frags f0, f1;
-  if (nk > 0) {
+  // The main loop, with the loads of stage kt+3 spread one per MFMA of the first
+  // k-step.  With K a multiple of the stage depth (the usual case) no stage has
+  // a K tail and the loads take the branch-free path.
+  auto run = [&](auto whole_c) {
+    constexpr bool WHOLE = decltype(whole_c)::value;
 #pragma unroll
-    for (int s = 0; s < DST - 1; ++s) issue(s);
+    for (int s = 0; s < DST - 1; ++s) issue(s, whole_c);
     wait_stage(0);
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
@@ -728,7 +732,7 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
       __builtin_amdgcn_sched_barrier(0);
       // stage kt+3 reuses the slot of stage kt-1, whose reads all came before
       // the previous barrier
-      issue(kt + DST - 1);
+      issue(kt + DST - 1, whole_c);
       frags(kt, 1, f1);
       mfmas(f0);
 #pragma unroll
@@ -738,7 +742,12 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
       }
       __builtin_amdgcn_sched_barrier(0);
-      wait_stage(kt + 1);
+      if (WHOLE) {
+        if (hi) wait_vmcnt<2 * (LA + LBH)>();
+        else wait_vmcnt<2 * (LA + LBL)>();
+      } else {
+        wait_stage(kt + 1);
+      }
       wait_lgkmcnt0();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -752,6 +761,10 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
+  };
+  if (nk > 0) {
+    if (p.K % DBK == 0) run(std::true_type{});
+    else run(std::false_type{});
   }
 
   gemm_store_tile<2, NBW, GATED, ACT>(p, acc, m0 + wm * 64, n0 + wn * (GATED ? WTN / 2 : WTN), l32, h2);
