@@ -8,8 +8,9 @@
 // [N, K] weight, as linear layers store it); the MLP runs it twice (act = GeLU
 // into the workspace, then act = identity).
 //
-// bf16: one workgroup per CU computes a 256 x BN tile (BN = 256, 192 or 128,
-// picked per launch so the tiles fill whole rounds of the chip) on
+// bf16: one workgroup per CU computes a 256 x BN tile (BN = 256, 192, 128 or,
+// k-contiguous weights only, 352; picked per launch so the tiles fill whole
+// rounds of the chip with the least padding) on
 // v_mfma_f32_32x32x16_bf16 blocks with f32 accumulators: 4 x 2 waves of
 // 64 x BN/2 (two waves per SIMD) for k-contiguous weights, 2 x 2 waves of
 // 128 x BN/2 (one wave per SIMD, accumulators in AGPRs) otherwise.
@@ -786,6 +787,180 @@ CHAIN_W8_KERNELS(silu, CHAIN_ACT_SILU)
 #undef CHAIN_W8_KERNELS
 #undef CHAIN_W8_KERNEL
 
+// Eight-wave variant with uneven wave columns, for tile widths that are an odd
+// number of 32-column blocks: a 256 x 32 (NB0 + NB1) tile as 4 x 2 waves of 64
+// rows; waves 0-3 take the first NB0 column blocks, waves 4-7 the other NB1.
+// Waves w and w+4 share a SIMD, so every SIMD still issues the MFMAs of NB0 +
+// NB1 blocks per k-step: the pipe stays as busy as with even columns.  With
+// NB0 = 6, NB1 = 5 (352 columns), N = 1376 is four tiles per 256 rows (2.3 %
+// padding) and M = 16384 one round of 256 tiles, where 192-wide tiles pad by
+// 11.6 % and take two rounds.  Six blocks of accumulators (192 registers) leave
+// no room for a second fragment set, so fragments are streamed: each is read
+// PD MFMAs before its first use, and the stage's wait and barrier sit PD MFMAs
+// before its end, after the last read of the stage and before the reads of the
+// next.  Ring, stage depth, swizzle, descriptors and k order are those of the
+// even eight-wave kernel, so both give the same bits.
+template <int NB0, int NB1, int ACT>
+__device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
+  constexpr int BN = 32 * (NB0 + NB1);
+  constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
+  static_assert(DST * STAGE <= 160 * 1024, "the ring must fit in LDS");
+  constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
+  constexpr int LA = BM / 16 / 8;               // 1 KB loads of A per wave and stage
+  constexpr int LBH = (NLB + 7) / 8, LBL = NLB / 8;   // of B: waves below NLB % 8 take LBH
+  __shared__ __attribute__((aligned(1024))) char lds[DST * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 3, wn = wave >> 2;
+  const bool hi = LBH == LBL || wave < NLB % 8;   // this wave takes LBH loads of B
+
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  constexpr int GM = 4;
+  const int g = t / (GM * tiles_n), fm = g * GM;
+  const int gmn = min(GM, tiles_m - fm), loc = t - g * GM * tiles_n;
+  const int m0 = (fm + loc % gmn) * BM, n0 = (loc / gmn) * BN;
+
+  const int ra = min(p.M - m0, BM), rb = min(p.N - n0, BN);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const __bf16 *)p.a + (int64_t)m0 * p.lda), 0,
+      (int)(((int64_t)(ra - 1) * p.lda + p.K) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const __bf16 *)p.b + (int64_t)n0 * p.b_sn), 0,
+      (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000);
+  // Lane i of a load fetches row i >> 2 of its 16-row group, logical chunk lc;
+  // load q of a wave covers the 16-row group wave + 8 q of its operand.
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t aoff[LA], boff[LBH];
+#pragma unroll
+  for (int q = 0; q < LA; ++q)
+    aoff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
+#pragma unroll
+  for (int q = 0; q < LBH; ++q)
+    boff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc;
+  const int nk = (p.K + DBK - 1) / DBK;
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  // Load q of this wave for stage kt (q < LA: A, else B) into ring slot kt % DST;
+  // past the last stage, stage 0 again into a slot nobody reads.  Whole stages
+  // carry the k offset in the scalar offset; in the K tail a chunk past K
+  // fetches k = K - 8 of its row instead.
+  auto issue_one = [&](int kt, int q, auto whole_c) {
+    char *sb = lds + (kt & (DST - 1)) * STAGE;
+    const int k0 = kt < nk ? kt * DBK : 0;
+    const bool whole = decltype(whole_c)::value || k0 + DBK <= p.K;
+    const uint32_t kv = whole ? 0u : 2u * (uint32_t)min(k0 + 8 * lc, p.K - 8) - 16u * lc;
+    const int ks = whole ? 2 * k0 : 0;
+    if (q < LA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(sb + (wave + 8 * q) * 1024), 16, aoff[q] + kv,
+                                               ks, 0, 0);
+    else if (q - LA < LBL || hi)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void *)(sb + A_BYTES + (wave + 8 * (q - LA)) * 1024), 16,
+                                               boff[q - LA] + kv, ks, 0, 0);
+  };
+  auto zero_tail = [&](int kt) {   // after stage kt (the K tail) has landed
+    if (kt * DBK + 8 * lc >= p.K) {
+      char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < LA; ++q) *(u32x4 *)(sb + (wave + 8 * q) * 1024) = z;
+#pragma unroll
+      for (int q = 0; q < LBH; ++q)
+        if (q < LBL || hi) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+    }
+  };
+  // this wave's loads of the oldest stage in flight have landed (the two
+  // stages after it may still be in flight)
+  auto wait_landed = [&]() {
+    if (hi) wait_vmcnt<2 * (LA + LBH)>();
+    else wait_vmcnt<2 * (LA + LBL)>();
+  };
+
+  const int sx = (l32 >> 2) & 3;
+  const int pc[2] = {(h2 ^ sx) * 16, ((2 + h2) ^ sx) * 16};
+  const int rowa = (wm * 64 + l32) * 64;
+
+  auto body = [&](auto nbw_c, int col0) {
+    constexpr int NBW = decltype(nbw_c)::value;
+    // MFMA m of a stage (m = 0 .. NM-1): k-step m / 2NBW, B block (m / 2) % NBW,
+    // A block m % 2.  The A pair and B block 0 of a k-step are read for its
+    // first MFMA, B block j for MFMA 2j.
+    constexpr int NM = 4 * NBW, PD = 4;
+    static_assert(PD % 2 == 0 && PD <= 2 * NBW, "reads run ahead within one k-step");
+    const int rowb = A_BYTES + (col0 + l32) * 64;
+    bf16x8 fa[2][2], fb[2][NBW];
+    f32x16 acc[2][NBW];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) acc[i][j] = f32x16{};
+    auto read_at = [&](const char *sb, int u) {   // the fragments first used at MFMA u
+      const int ks = u / (2 * NBW), r = u % (2 * NBW);
+      const char *b = sb + pc[ks];
+      if (r == 0) {
+        fa[ks][0] = *(const bf16x8 *)(b + rowa);
+        fa[ks][1] = *(const bf16x8 *)(b + rowa + 2048);
+      }
+      if (r % 2 == 0) fb[ks][r / 2] = *(const bf16x8 *)(b + rowb + (r / 2) * 2048);
+    };
+    auto run = [&](auto whole_c) {
+      constexpr bool WHOLE = decltype(whole_c)::value;
+#pragma unroll
+      for (int s = 0; s < DST - 1; ++s)
+#pragma unroll
+        for (int q = 0; q < LA + LBH; ++q) issue_one(s, q, whole_c);
+      wait_landed();
+      if (!WHOLE && DBK > p.K) zero_tail(0);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int u = 0; u < PD; ++u) read_at(lds, u);
+      for (int kt = 0; kt < nk; ++kt) {
+        const char *cur = lds + (kt & (DST - 1)) * STAGE;
+        const char *nxt = lds + ((kt + 1) & (DST - 1)) * STAGE;   // past the last stage: an unused slot
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if (m == NM - PD) {
+            // every read of this stage is issued: once they are back, stage
+            // kt+1 has landed and all waves are here, its slot may be refilled
+            wait_lgkmcnt0();
+            wait_landed();
+            if (!WHOLE && kt + 1 < nk && (kt + 1) * DBK + DBK > p.K) zero_tail(kt + 1);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (m + PD < NM) read_at(cur, m + PD);
+          else read_at(nxt, m + PD - NM);
+          // stage kt+3 refills the slot of stage kt-1, released at its barrier
+          if (m < LA + LBH) issue_one(kt + DST - 1, m, whole_c);
+          const int ks = m / (2 * NBW), j = (m / 2) % NBW, i = m % 2;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
+    };
+    if (nk > 0) {
+      if (p.K % DBK == 0) run(std::true_type{});
+      else run(std::false_type{});
+    }
+    gemm_store_tile<2, NBW, false, ACT>(p, acc, m0 + wm * 64, n0 + col0, l32, h2);
+  };
+  if (wn == 0) body(std::integral_constant<int, NB0>{}, 0);
+  else body(std::integral_constant<int, NB1>{}, 32 * NB0);
+}
+
+#define CHAIN_W8R_KERNEL(NAME, NB0, NB1, ACT)                                                 \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
+  void NAME(const GemmParams p) { gemm_bf16_w8r<NB0, NB1, ACT>(p); }
+CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_erf, 6, 5, CHAIN_ACT_GELU_ERF)
+CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_tanh, 6, 5, CHAIN_ACT_GELU_TANH)
+CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_id, 6, 5, CHAIN_ACT_IDENTITY)
+CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_silu, 6, 5, CHAIN_ACT_SILU)
+#undef CHAIN_W8R_KERNEL
+
 // f32 inputs: 128 x 128 x 32 tiles on v_mfma_f32_32x32x2_f32 (A: lane holds
 // A[m][k0 + h2], B: lane holds B[k0 + h2][n]); exact f32 products, f32
 // accumulation.
@@ -868,13 +1043,13 @@ void launch_bf16_width(const GemmParams &p, int nbw, hipStream_t stream) {
   else launch_bf16<2>(p, stream);
 }
 
-// The eight-wave kernels address a tile's rows with 32-bit byte offsets.
-bool w8_fits(const GemmParams &p, int nbw, bool gated) {
-  const int obn = gated ? 32 * nbw : 64 * nbw;   // output columns per tile
+// The eight- and four-wave kernels address a tile's rows with 32-bit byte offsets.
+bool rows_fit32(const GemmParams &p, int obn) {
   const int64_t span_a = ((int64_t)(min(p.M, BM) - 1) * p.lda + p.K) * 2;
   const int64_t span_b = ((int64_t)(min(p.N, obn) - 1) * p.b_sn + p.K) * 2;
   return span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
 }
+bool w8_fits(const GemmParams &p, int nbw, bool gated) { return rows_fit32(p, gated ? 32 * nbw : 64 * nbw); }
 
 // Gated: 32 * nbw output columns per tile; nbw 4 unless 2 fills the chip's
 // rounds with less work per CU.
@@ -922,6 +1097,15 @@ void launch_w8(const GemmParams &p, int nbw, hipStream_t stream) {
   hipLaunchKernelGGL(ks[nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
 }
 
+// 352-wide tiles: 11 column blocks, 6 + 5 over the two wave columns.
+void launch_w8r(const GemmParams &p, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 351) / 352);
+  typedef void (*Kern)(const GemmParams);
+  static const Kern ks[4] = {gemm_bf16_w8r_kernel_11_erf, gemm_bf16_w8r_kernel_11_tanh, gemm_bf16_w8r_kernel_11_id,
+                             gemm_bf16_w8r_kernel_11_silu};
+  hipLaunchKernelGGL(ks[p.act], dim3(tiles), dim3(512), 0, stream, p);
+}
+
 int compute_units() {
   static thread_local int dev_cached = -1, cus = 256;
   int dev = 0;
@@ -937,15 +1121,21 @@ int compute_units() {
 }  // namespace
 
 // Tile width for the bf16 path: the one that minimises rounds x tile width
-// (one workgroup per CU; the time of a tile grows with its width).
-int gemm_bf16_block_cols(int M, int N, int cus) {
+// (one workgroup per CU; the time of a tile grows with its width).  Eight-wave
+// tiles are 64 x nbw wide (nbw 4, 3, 2); with wide = true the 352-wide tiles
+// of the uneven eight-wave kernel are a candidate too, taken only when they
+// cost strictly less.  Returns nbw, or 11 for the 352-wide tiles.
+int gemm_bf16_block_cols(int M, int N, int cus, bool wide) {
   int best = 4;
   int64_t best_cost = INT64_MAX;
-  for (int nbw = 4; nbw >= 2; --nbw) {
-    const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + 64 * nbw - 1) / (64 * nbw));
-    const int64_t cost = ((tiles + cus - 1) / cus) * nbw;
-    if (cost < best_cost) best = nbw, best_cost = cost;
-  }
+  const int64_t tm = (M + BM - 1) / BM;
+  auto cost = [&](int width) {
+    const int64_t tiles = tm * ((N + width - 1) / width);
+    return ((tiles + cus - 1) / cus) * width;
+  };
+  for (int nbw = 4; nbw >= 2; --nbw)
+    if (cost(64 * nbw) < best_cost) best = nbw, best_cost = cost(64 * nbw);
+  if (wide && cost(352) < best_cost) best = 11;
   return best;
 }
 
@@ -955,8 +1145,12 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
     if (dtype != CHAIN_BF16 || p.b_sk != 1) return hipErrorInvalidValue;
     launch_dtl_gated(p, compute_units(), stream);
   } else if (dtype == CHAIN_BF16) {
-    const int nbw = gemm_bf16_block_cols(p.M, p.N, compute_units());
-    if (p.b_sk == 1) {
+    const bool k_contig = p.b_sk == 1;
+    const int choice = gemm_bf16_block_cols(p.M, p.N, compute_units(), k_contig);
+    const int nbw = choice == 11 ? 4 : choice;
+    if (k_contig && choice == 11 && rows_fit32(p, 352)) {
+      launch_w8r(p, stream);
+    } else if (k_contig) {
       if (w8_fits(p, nbw, false)) launch_w8(p, nbw, stream);
       else launch_dtl(p, nbw, stream);
     } else {

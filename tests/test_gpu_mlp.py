@@ -56,6 +56,36 @@ def test_mlp_ffn_shard_m16384_sampled(kmajor):
     assert err <= TOL_BF16
 
 
+def _rounds_x_width(M, N, width, cus=256):
+    tiles = -(-M // 256) * -(-N // width)
+    return -(-tiles // cus) * width
+
+
+def test_mlp_wide_tiles_ragged():
+    """An X.W1 whose inner width takes the 352-wide uneven tiles on a 256-CU chip
+    (one round, where 128-, 192- and 256-wide tiles need two or three), with a
+    ragged last row tile, a ragged last column tile and a K tail; k-major weights
+    take those tiles, row-major ones the register-staged kernel, and both must
+    give the same bits."""
+    M, K, N, K2 = 8092, 4104, 2792, 512
+    assert _rounds_x_width(M, N, 352) < min(_rounds_x_width(M, N, w) for w in (128, 192, 256))
+    dev = device()
+    if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
+        pytest.skip("the tile choice asserted here assumes 256 compute units")
+    x, w1, w2 = gen_mlp(M, K, N, K2, dtype="bf16", amp_x=1.0, amp_w=0.02, seed=53)
+    announce(f"mlp wide tiles M{M} K{K} N{N} K2{K2}")
+    xd, w1d, w2d = x.to(dev), w1.to(dev), w2.to(dev)
+    o_row = chain.mlp_fwd(xd, w1d, w2d, act="gelu_erf")
+    o_k = chain.mlp_fwd(xd, _kmajor(w1d), _kmajor(w2d), act="gelu_erf")
+    torch.cuda.synchronize()
+    assert torch.equal(o_row, o_k)
+    rows = sample_rows(M, 120, 53, extra=(0, 255, 256, 7935, 7936, M - 1))
+    ref = oracle.mlp(f64(x[rows]), f64(w1), f64(w2), "gelu_erf")
+    err = max_abs(f64(o_k.cpu()[rows]), ref)
+    print(f"max-abs {err:.3e} over {len(rows)} rows")
+    assert err <= TOL_BF16
+
+
 def test_mlp_shard_sum_equals_whole():
     """Summing the outputs of inner-dimension shards gives the unsharded chain."""
     dev = device()
