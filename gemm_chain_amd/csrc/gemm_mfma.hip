@@ -19,10 +19,13 @@
 // Two ways of feeding LDS, by weight layout:
 //  - k-contiguous B: loads that write LDS directly fill a ring of four
 //    k-stages of 32, fetched three stages ahead, rows XOR-swizzled instead of
-//    padded.  gemm_bf16_w8_kernel_NBW runs eight waves (two per SIMD) of
-//    64 x BN/2 with buffer loads; gemm_bf16_dtl_kernel_NBW, the same ring with
-//    four waves of 128 x BN/2, serves operands whose 256-row tiles span 2 GiB
-//    or more (beyond 32-bit buffer offsets);
+//    padded.  gemm_bf16_w8r_kernel_NB runs eight waves (two per SIMD) of 64
+//    rows, the two wave columns taking NB/2 32-column blocks each (6 + 5 for
+//    NB = 11), with buffer loads and streamed fragments;
+//    gemm_bf16_w8_gated_kernel_NBW feeds the gated product the same way;
+//    gemm_bf16_dtl_kernel_NBW, the same ring with four waves of 128 x BN/2,
+//    serves operands whose 256-row tiles span 2 GiB or more (beyond 32-bit
+//    buffer offsets);
 //  - n-contiguous B (gemm_bf16_kernel<NBW>): k-tiles of 64 staged through
 //    registers into two LDS buffers; A as [256][64 + 8], B as [64][BN' + 32]
 //    read with ds_read_b64_tr_b16.
@@ -574,9 +577,9 @@ CHAIN_DTL_KERNELS(silu, CHAIN_ACT_SILU)
 #undef CHAIN_DTL_KERNELS
 #undef CHAIN_DTL_KERNEL
 
-// Eight-wave variant of the k-contiguous path (two waves per SIMD): a 256 x BN
-// tile as 4 x 2 waves of 64 x BN/2, each a 2 x NBW grid of 32 x 32 blocks with
-// f32 accumulators in registers.  The ring, the stage depth, the swizzle and
+// Eight-wave kernel of the gated k-contiguous path (two waves per SIMD): a
+// 256 x BN tile as 4 x 2 waves of 64 x BN/2, each a 2 x NBW grid of 32 x 32
+// blocks with f32 accumulators in registers.  The ring, the stage depth, the swizzle and
 // the k order are those of gemm_bf16_dtl (so both give the same bits); the
 // loads are buffer loads that write LDS directly, addressed by a descriptor
 // over the tile's rows (32-bit offsets: the host picks this kernel only when
@@ -775,9 +778,6 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
   void NAME(const GemmParams p) { gemm_bf16_w8<NBW, GATED, ACT>(p); }
 #define CHAIN_W8_KERNELS(SUFFIX, ACT)                                    \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_2_##SUFFIX, 2, false, ACT)         \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_3_##SUFFIX, 3, false, ACT)         \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_kernel_4_##SUFFIX, 4, false, ACT)         \
   CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_2_##SUFFIX, 2, true, ACT)    \
   CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_4_##SUFFIX, 4, true, ACT)
 CHAIN_W8_KERNELS(erf, CHAIN_ACT_GELU_ERF)
@@ -787,19 +787,20 @@ CHAIN_W8_KERNELS(silu, CHAIN_ACT_SILU)
 #undef CHAIN_W8_KERNELS
 #undef CHAIN_W8_KERNEL
 
-// Eight-wave variant with uneven wave columns, for tile widths that are an odd
-// number of 32-column blocks: a 256 x 32 (NB0 + NB1) tile as 4 x 2 waves of 64
-// rows; waves 0-3 take the first NB0 column blocks, waves 4-7 the other NB1.
-// Waves w and w+4 share a SIMD, so every SIMD still issues the MFMAs of NB0 +
-// NB1 blocks per k-step: the pipe stays as busy as with even columns.  With
+// Eight-wave kernel of the non-gated k-contiguous path: a 256 x 32 (NB0 + NB1)
+// tile as 4 x 2 waves of 64 rows; waves 0-3 take the first NB0 column blocks,
+// waves 4-7 the other NB1 (NB0 = NB1 for 128-, 192- and 256-wide tiles).  The
+// columns may split unevenly: waves w and w+4 share a SIMD, so every SIMD
+// still issues the MFMAs of NB0 + NB1 blocks per k-step.  With
 // NB0 = 6, NB1 = 5 (352 columns), N = 1376 is four tiles per 256 rows (2.3 %
 // padding) and M = 16384 one round of 256 tiles, where 192-wide tiles pad by
 // 11.6 % and take two rounds.  Six blocks of accumulators (192 registers) leave
-// no room for a second fragment set, so fragments are streamed: each is read
+// no room for a second fragment set, so fragments are streamed (at every width:
+// it also beats a double-buffered k-step by about 1 % at 256): each is read
 // PD MFMAs before its first use, and the stage's wait and barrier sit PD MFMAs
 // before its end, after the last read of the stage and before the reads of the
 // next.  Ring, stage depth, swizzle, descriptors and k order are those of the
-// even eight-wave kernel, so both give the same bits.
+// gated and four-wave kernels, so all give the same bits.
 template <int NB0, int NB1, int ACT>
 __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   constexpr int BN = 32 * (NB0 + NB1);
@@ -955,10 +956,16 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
 #define CHAIN_W8R_KERNEL(NAME, NB0, NB1, ACT)                                                 \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
   void NAME(const GemmParams p) { gemm_bf16_w8r<NB0, NB1, ACT>(p); }
-CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_erf, 6, 5, CHAIN_ACT_GELU_ERF)
-CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_tanh, 6, 5, CHAIN_ACT_GELU_TANH)
-CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_id, 6, 5, CHAIN_ACT_IDENTITY)
-CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_silu, 6, 5, CHAIN_ACT_SILU)
+#define CHAIN_W8R_KERNELS(SUFFIX, ACT)                                 \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_4_##SUFFIX, 2, 2, ACT)         \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_6_##SUFFIX, 3, 3, ACT)         \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_8_##SUFFIX, 4, 4, ACT)         \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_##SUFFIX, 6, 5, ACT)
+CHAIN_W8R_KERNELS(erf, CHAIN_ACT_GELU_ERF)
+CHAIN_W8R_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
+CHAIN_W8R_KERNELS(id, CHAIN_ACT_IDENTITY)
+CHAIN_W8R_KERNELS(silu, CHAIN_ACT_SILU)
+#undef CHAIN_W8R_KERNELS
 #undef CHAIN_W8R_KERNEL
 
 // f32 inputs: 128 x 128 x 32 tiles on v_mfma_f32_32x32x2_f32 (A: lane holds
@@ -1087,23 +1094,19 @@ void launch_dtl(const GemmParams &p, int nbw, hipStream_t stream) {
   hipLaunchKernelGGL(ks[nbw - 2][p.act], dim3(tiles), dim3(256), 0, stream, p);
 }
 
+// Non-gated eight-wave tiles: nbw = 2, 3, 4 (128, 192, 256 columns, even wave
+// columns) or 11 (352 columns, 6 + 5).
 void launch_w8(const GemmParams &p, int nbw, hipStream_t stream) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 64 * nbw - 1) / (64 * nbw));
+  const int width = nbw == 11 ? 352 : 64 * nbw;
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + width - 1) / width);
   typedef void (*Kern)(const GemmParams);
-  static const Kern ks[3][4] = {
-      {gemm_bf16_w8_kernel_2_erf, gemm_bf16_w8_kernel_2_tanh, gemm_bf16_w8_kernel_2_id, gemm_bf16_w8_kernel_2_silu},
-      {gemm_bf16_w8_kernel_3_erf, gemm_bf16_w8_kernel_3_tanh, gemm_bf16_w8_kernel_3_id, gemm_bf16_w8_kernel_3_silu},
-      {gemm_bf16_w8_kernel_4_erf, gemm_bf16_w8_kernel_4_tanh, gemm_bf16_w8_kernel_4_id, gemm_bf16_w8_kernel_4_silu}};
-  hipLaunchKernelGGL(ks[nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
-}
-
-// 352-wide tiles: 11 column blocks, 6 + 5 over the two wave columns.
-void launch_w8r(const GemmParams &p, hipStream_t stream) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 351) / 352);
-  typedef void (*Kern)(const GemmParams);
-  static const Kern ks[4] = {gemm_bf16_w8r_kernel_11_erf, gemm_bf16_w8r_kernel_11_tanh, gemm_bf16_w8r_kernel_11_id,
-                             gemm_bf16_w8r_kernel_11_silu};
-  hipLaunchKernelGGL(ks[p.act], dim3(tiles), dim3(512), 0, stream, p);
+  static const Kern ks[4][4] = {
+      {gemm_bf16_w8r_kernel_4_erf, gemm_bf16_w8r_kernel_4_tanh, gemm_bf16_w8r_kernel_4_id, gemm_bf16_w8r_kernel_4_silu},
+      {gemm_bf16_w8r_kernel_6_erf, gemm_bf16_w8r_kernel_6_tanh, gemm_bf16_w8r_kernel_6_id, gemm_bf16_w8r_kernel_6_silu},
+      {gemm_bf16_w8r_kernel_8_erf, gemm_bf16_w8r_kernel_8_tanh, gemm_bf16_w8r_kernel_8_id, gemm_bf16_w8r_kernel_8_silu},
+      {gemm_bf16_w8r_kernel_11_erf, gemm_bf16_w8r_kernel_11_tanh, gemm_bf16_w8r_kernel_11_id,
+       gemm_bf16_w8r_kernel_11_silu}};
+  hipLaunchKernelGGL(ks[nbw == 11 ? 3 : nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
 }
 
 int compute_units() {
@@ -1148,10 +1151,8 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
     const bool k_contig = p.b_sk == 1;
     const int choice = gemm_bf16_block_cols(p.M, p.N, compute_units(), k_contig);
     const int nbw = choice == 11 ? 4 : choice;
-    if (k_contig && choice == 11 && rows_fit32(p, 352)) {
-      launch_w8r(p, stream);
-    } else if (k_contig) {
-      if (w8_fits(p, nbw, false)) launch_w8(p, nbw, stream);
+    if (k_contig) {
+      if (rows_fit32(p, choice == 11 ? 352 : 64 * nbw)) launch_w8(p, choice, stream);
       else launch_dtl(p, nbw, stream);
     } else {
       launch_bf16_width(p, nbw, stream);
