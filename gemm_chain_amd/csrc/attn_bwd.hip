@@ -12,9 +12,12 @@
 //
 // Three kernels, no atomics (every output element is written once, so reruns
 // give identical bits):
-//  - rowdot: per query row, D_i and LSE_i * log2(e) into the workspace, in
-//    blocks of 16 rows [16 x LSE*log2e | 16 x D], rows padded to a multiple of
-//    64 with (+inf, 0) so that padding rows get probability 0.
+//  - rowdot: per query row, D_i and -LSE_i * log2(e) into the workspace, in
+//    blocks of 16 rows [16 x -LSE*log2e | 16 x D], rows padded to a multiple of
+//    64 with (-inf, 0) so that padding rows get probability 0.  The scores are
+//    formed in base 2 from bf16 operands scaled by scale * log2(e) (Q in dq,
+//    as in the forward; K in dkdv), and each S accumulator starts from
+//    -LSE * log2(e) (-inf where masked), so P is one exp2 of it.
 //  - dq: eight waves (two per SIMD) take 32-row query blocks of WH heads of one
 //    key/value head and walk the visible 64-key tiles.  Per tile and wave:
 //    S^T = K.Q^T and dP^T = V.dO^T (Q and dO fragments stay in registers, each
@@ -57,8 +60,11 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Transposing LDS read: in each group of 16 lanes, lane i receives element i%4
-// of the 4-element rows addressed by lanes 4e + i/4, e = 0..3.
-__device__ inline i16x4 ds_read_tr(const char *p) {
+// of the 4-element rows addressed by lanes 4e + i/4, e = 0..3.  The restrict
+// qualifier tells the compiler the read does not alias the direct-to-LDS loads
+// in flight; without it, it waits for all of them (vmcnt(0)) before the read,
+// which empties the three-tile prefetch ring at every key block.
+__device__ inline i16x4 ds_read_tr(const char *__restrict__ p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
@@ -147,7 +153,7 @@ struct FragOffsets {
 
 __device__ inline int padded_rows(int S) { return (S + kRowPad - 1) / kRowPad * kRowPad; }
 
-// Float index of row r's LSE*log2e in its head's workspace block; D_i is 16 further.
+// Float index of row r's -LSE*log2e in its head's workspace block; D_i is 16 further.
 __device__ inline int rv_index(int r) { return (r >> 4) * 32 + (r & 15); }
 
 // ---- D_i and LSE_i * log2(e) -------------------------------------------------
@@ -172,13 +178,13 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const AttnBwdParams p) {
 #pragma unroll
   for (int w = CPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, CPR);
   if (row < rows && c == 0) {
-    float l2 = INFINITY;   // padding rows and rows without a visible key: probability 0
+    float nl2 = -INFINITY;   // padding rows and rows without a visible key: probability 0
     if (real) {
       const float lse = p.lse[b * p.l_sb + h * p.l_sh + (int64_t)s * p.l_ss];
-      if (lse != -INFINITY) l2 = lse * kLog2e;
+      if (lse != -INFINITY) nl2 = -lse * kLog2e;
     }
     float *blk = p.rowv + bh * Sp * 2;
-    blk[rv_index(s)] = l2;
+    blk[rv_index(s)] = nl2;
     blk[rv_index(s) + 16] = real ? acc : 0.f;
   }
 }
@@ -245,15 +251,21 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
     {
       const __bf16 *qr = (const __bf16 *)p.q + b * p.q_sb + head * p.q_sh + (int64_t)rr * p.q_ss + 8 * h2;
       const __bf16 *gr = (const __bf16 *)p.dout + b * p.do_sb + head * p.do_sh + (int64_t)rr * p.do_ss + 8 * h2;
+      // Q times scale * log2(e), rounded to bf16 (as the forward forms its scores)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = row_ok ? *(const bf16x8 *)(qr + 16 * ks) : bf16x8{};
+        const bf16x8 raw = row_ok ? *(const bf16x8 *)(qr + 16 * ks) : bf16x8{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * c);
         dof[ks] = row_ok ? *(const bf16x8 *)(gr + 16 * ks) : bf16x8{};
       }
     }
     const float *rv = p.rowv + ((int64_t)b * p.Hq + head) * Sp * 2;
-    const float lse2 = row_ok ? rv[rv_index(rr)] : INFINITY;
+    const float nl2 = row_ok ? rv[rv_index(rr)] : -INFINITY;
     const float drow = row_ok ? rv[rv_index(rr) + 16] : 0.f;
+    f32x16 sinit;   // the S accumulators start from -LSE * log2(e) of the lane's query
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sinit[r] = nl2;
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -279,17 +291,23 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
       for (int kb = 0; kb < 2; ++kb) {
         if (p.causal && k0 + 32 * kb > w_qmax) continue;
         const char *kt_ = sb + kb * 32 * RB;
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s, dp = f32x16{};
         run_b128<KS>([&](int i) { return kt_ + fo.aoff[i]; },
-                     [&](int i, bf16x8 a) { s = mfma32(a, qf[i], s); });
+                     [&](int i, bf16x8 a) { s = mfma32(a, qf[i], i == 0 ? sinit : s); });
         run_b128<KS>([&](int i) { return kt_ + TB + fo.aoff[i]; },
                      [&](int i, bf16x8 a) { dp = mfma32(a, dof[i], dp); });
-        // lane (h2, l32) holds key k0 + 32kb + 8(r/4) + 4h2 + r%4 of query my_row
+        // lane (h2, l32) holds key k0 + 32kb + 8(r/4) + 4h2 + r%4 of query my_row;
+        // keys past the limit get score -inf, so probability 0 (a uniform
+        // branch: full tiles skip the compares)
+        if (!full) {
+          const int rel = lim - (k0 + 32 * kb + 4 * h2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = 8 * (r >> 2) + (r & 3) <= rel ? s[r] : -INFINITY;
+        }
         bf16x8 dsk[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-          if (!full) x = k0 + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3) <= lim ? x : 0.f;
+          const float x = __builtin_amdgcn_exp2f(s[r]);
           dsk[r >> 3][r & 7] = (__bf16)(x * (dp[r] - drow));
         }
         // dQ^T += K^T . dS^T over this block's 32 keys
@@ -384,9 +402,12 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
     {
       const __bf16 *kr = (const __bf16 *)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)kk * p.k_ss + 8 * h2;
       const __bf16 *vr = (const __bf16 *)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)kk * p.v_ss + 8 * h2;
+      // K times scale * log2(e), rounded to bf16: the scores come out in base 2
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        kf[ks] = key_ok ? *(const bf16x8 *)(kr + 16 * ks) : bf16x8{};
+        const bf16x8 raw = key_ok ? *(const bf16x8 *)(kr + 16 * ks) : bf16x8{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[ks][e] = (__bf16)((float)raw[e] * c);
         vf[ks] = key_ok ? *(const bf16x8 *)(vr + 16 * ks) : bf16x8{};
       }
     }
@@ -429,24 +450,36 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
       const float *rv = (const float *)(sb + 2 * TB);
       // query q0 + 32qb + 8g + 4h2 + e sees key my_key iff 32qb + 8g + e >= qoff
       const int qoff = p.causal ? my_key - q0 - 4 * h2 : -(1 << 30);
-      f32x16 s[2], dp[2];
+      f32x16 s[2], dp[2], sinit[2];
       bf16x8 pk[2][2], dsk[2][2];
-      f32x4 l4[2][4], d4[2][4];
+      f32x4 d4[2][4];
+      // S accumulator element r of block qb belongs to query 8(r/4) + 4h2 + r%4
+      // of the block; it starts from that query's -LSE * log2(e), or -inf where
+      // the key is not visible (a uniform branch: only steps that cross the
+      // diagonal compare)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ri = rv_index(32 * qb + 8 * g + 4 * h2);
-          l4[qb][g] = *(const f32x4 *)(rv + ri);
+          const f32x4 l4 = *(const f32x4 *)(rv + ri);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sinit[qb][4 * g + e] = l4[e];
           d4[qb][g] = *(const f32x4 *)(rv + ri + 16);
         }
+      if (p.causal && q0 < kw0 + 31) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[qb] = f32x16{}, dp[qb] = f32x16{};
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sinit[qb][r] = 32 * qb + 8 * (r >> 2) + (r & 3) >= qoff ? sinit[qb][r] : -INFINITY;
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) dp[qb] = f32x16{};
       // P and dS of element r (query 8(r/4) + 4h2 + r%4 of the block) of block qb
       auto elem = [&](int qb, int r) {
         const int g = r >> 2, e = r & 3;
-        float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l4[qb][g][e]));
-        x = 32 * qb + 8 * g + e >= qoff ? x : 0.f;
+        const float x = __builtin_amdgcn_exp2f(s[qb][r]);
         pk[qb][r >> 3][r & 7] = (__bf16)x;
         dsk[qb][r >> 3][r & 7] = (__bf16)(x * (dp[qb][r] - d4[qb][g][e]));
       };
@@ -465,7 +498,7 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
           const bf16x8 fa = f[i % A];
           if (i + A < NM) f[i % A] = *(const bf16x8 *)addr(i + A);
           if (i & 1) dp[qb] = mfma32(fa, vf[i >> 1], dp[qb]);
-          else s[qb] = mfma32(fa, kf[i >> 1], s[qb]);
+          else s[qb] = mfma32(fa, kf[i >> 1], i == 0 ? sinit[qb] : s[qb]);
           side(i);
           __builtin_amdgcn_sched_barrier(0);
         }
