@@ -12,12 +12,13 @@
 //
 // Three kernels, no atomics (every output element is written once, so reruns
 // give identical bits):
-//  - rowdot: per query row, D_i and -LSE_i * log2(e) into the workspace, in
-//    blocks of 16 rows [16 x -LSE*log2e | 16 x D], rows padded to a multiple of
-//    64 with (-inf, 0) so that padding rows get probability 0.  The scores are
-//    formed in base 2 from bf16 operands scaled by scale * log2(e) (Q in dq,
-//    as in the forward; K in dkdv), and each S accumulator starts from
-//    -LSE * log2(e) (-inf where masked), so P is one exp2 of it.
+//  - rowdot: per query row, -D_i and -LSE_i * log2(e) into the workspace, in
+//    blocks of 16 rows [16 x -LSE*log2e | 16 x -D], rows padded to a multiple
+//    of 64 with (-inf, 0) so that padding rows get probability 0.  The scores
+//    are formed in base 2 from bf16 operands scaled by scale * log2(e) (Q in
+//    dq, as in the forward; K in dkdv); each S accumulator starts from
+//    -LSE * log2(e) (-inf where masked) and each dP accumulator from -D, so P
+//    is one exp2 and dS one product.
 //  - dq: eight waves (two per SIMD) take 32-row query blocks of WH heads of one
 //    key/value head and walk the visible 64-key tiles.  Per tile and wave:
 //    S^T = K.Q^T and dP^T = V.dO^T (Q and dO fragments stay in registers, each
@@ -153,7 +154,7 @@ struct FragOffsets {
 
 __device__ inline int padded_rows(int S) { return (S + kRowPad - 1) / kRowPad * kRowPad; }
 
-// Float index of row r's -LSE*log2e in its head's workspace block; D_i is 16 further.
+// Float index of row r's -LSE*log2e in its head's workspace block; -D_i is 16 further.
 __device__ inline int rv_index(int r) { return (r >> 4) * 32 + (r & 15); }
 
 // ---- D_i and LSE_i * log2(e) -------------------------------------------------
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const AttnBwdParams p) {
     }
     float *blk = p.rowv + bh * Sp * 2;
     blk[rv_index(s)] = nl2;
-    blk[rv_index(s) + 16] = real ? acc : 0.f;
+    blk[rv_index(s) + 16] = real ? -acc : 0.f;
   }
 }
 
@@ -262,8 +263,10 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
     }
     const float *rv = p.rowv + ((int64_t)b * p.Hq + head) * Sp * 2;
     const float nl2 = row_ok ? rv[rv_index(rr)] : -INFINITY;
-    const float drow = row_ok ? rv[rv_index(rr) + 16] : 0.f;
-    f32x16 sinit;   // the S accumulators start from -LSE * log2(e) of the lane's query
+    const float nd = row_ok ? rv[rv_index(rr) + 16] : 0.f;
+    // the S accumulators start from -LSE * log2(e) of the lane's query (a -D
+    // start for dP as well would cost 16 more registers than the kernel has)
+    f32x16 sinit;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sinit[r] = nl2;
     f32x16 acc[DB];
@@ -308,7 +311,7 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = __builtin_amdgcn_exp2f(s[r]);
-          dsk[r >> 3][r & 7] = (__bf16)(x * (dp[r] - drow));
+          dsk[r >> 3][r & 7] = (__bf16)(x * (dp[r] + nd));
         }
         // dQ^T += K^T . dS^T over this block's 32 keys
         run_tr<2 * DB>([&](int i) { return kt_ + (i & 1) * 16 * RB + fo.tlo[i >> 1]; },
@@ -450,22 +453,21 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
       const float *rv = (const float *)(sb + 2 * TB);
       // query q0 + 32qb + 8g + 4h2 + e sees key my_key iff 32qb + 8g + e >= qoff
       const int qoff = p.causal ? my_key - q0 - 4 * h2 : -(1 << 30);
-      f32x16 s[2], dp[2], sinit[2];
+      f32x16 s[2], dp[2], sinit[2], dpinit[2];
       bf16x8 pk[2][2], dsk[2][2];
-      f32x4 d4[2][4];
-      // S accumulator element r of block qb belongs to query 8(r/4) + 4h2 + r%4
-      // of the block; it starts from that query's -LSE * log2(e), or -inf where
-      // the key is not visible (a uniform branch: only steps that cross the
-      // diagonal compare)
+      // Accumulator element r of block qb belongs to query 8(r/4) + 4h2 + r%4 of
+      // the block: S starts from that query's -LSE * log2(e), or -inf where the
+      // key is not visible (a uniform branch: only steps that cross the
+      // diagonal compare), dP from its -D
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ri = rv_index(32 * qb + 8 * g + 4 * h2);
           const f32x4 l4 = *(const f32x4 *)(rv + ri);
+          const f32x4 d4 = *(const f32x4 *)(rv + ri + 16);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sinit[qb][4 * g + e] = l4[e];
-          d4[qb][g] = *(const f32x4 *)(rv + ri + 16);
+          for (int e = 0; e < 4; ++e) sinit[qb][4 * g + e] = l4[e], dpinit[qb][4 * g + e] = d4[e];
         }
       if (p.causal && q0 < kw0 + 31) {
 #pragma unroll
@@ -474,14 +476,11 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
           for (int r = 0; r < 16; ++r)
             sinit[qb][r] = 32 * qb + 8 * (r >> 2) + (r & 3) >= qoff ? sinit[qb][r] : -INFINITY;
       }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) dp[qb] = f32x16{};
       // P and dS of element r (query 8(r/4) + 4h2 + r%4 of the block) of block qb
       auto elem = [&](int qb, int r) {
-        const int g = r >> 2, e = r & 3;
         const float x = __builtin_amdgcn_exp2f(s[qb][r]);
         pk[qb][r >> 3][r & 7] = (__bf16)x;
-        dsk[qb][r >> 3][r & 7] = (__bf16)(x * (dp[qb][r] - d4[qb][g][e]));
+        dsk[qb][r >> 3][r & 7] = (__bf16)(x * dp[qb][r]);
       };
       constexpr int NM = 2 * KS;          // MFMAs per phase (= 4 * DB)
       constexpr int EPM = 16 / NM;        // softmax elements per MFMA
@@ -497,7 +496,7 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
         for (int i = 0; i < NM; ++i) {
           const bf16x8 fa = f[i % A];
           if (i + A < NM) f[i % A] = *(const bf16x8 *)addr(i + A);
-          if (i & 1) dp[qb] = mfma32(fa, vf[i >> 1], dp[qb]);
+          if (i & 1) dp[qb] = mfma32(fa, vf[i >> 1], i == 1 ? dpinit[qb] : dp[qb]);
           else s[qb] = mfma32(fa, kf[i >> 1], i == 0 ? sinit[qb] : s[qb]);
           side(i);
           __builtin_amdgcn_sched_barrier(0);
