@@ -1123,18 +1123,19 @@ int compute_units() {
 
 }  // namespace
 
-// Tile width for the bf16 path: the one that minimises rounds x tile width
-// (one workgroup per CU; the time of a tile grows with its width).  Eight-wave
-// tiles are 64 x nbw wide (nbw 4, 3, 2); with wide = true the 352-wide tiles
-// of the uneven eight-wave kernel are a candidate too, taken only when they
-// cost strictly less.  Returns nbw, or 11 for the 352-wide tiles.
+// Tile width for the bf16 path: the one that minimises rounds x (tile width +
+// 64), one workgroup per CU; the time of a round grows with the tile width,
+// plus a part that does not (its first stage loads and its output stores, about
+// what 64 columns of MFMAs take at the FFN shard's shapes).  Eight-wave tiles
+// are 64 x nbw wide (nbw 4, 3, 2); with wide = true the 352-wide tiles of the
+// uneven split are a candidate too.  Returns nbw, or 11 for 352 columns.
 int gemm_bf16_block_cols(int M, int N, int cus, bool wide) {
   int best = 4;
   int64_t best_cost = INT64_MAX;
   const int64_t tm = (M + BM - 1) / BM;
   auto cost = [&](int width) {
     const int64_t tiles = tm * ((N + width - 1) / width);
-    return ((tiles + cus - 1) / cus) * width;
+    return ((tiles + cus - 1) / cus) * (width + 64);
   };
   for (int nbw = 4; nbw >= 2; --nbw)
     if (cost(64 * nbw) < best_cost) best = nbw, best_cost = cost(64 * nbw);

@@ -57,8 +57,9 @@ def test_mlp_ffn_shard_m16384_sampled(kmajor):
 
 
 def _rounds_x_width(M, N, width, cus=256):
+    """The library's tile-width cost: rounds x (width + 64)."""
     tiles = -(-M // 256) * -(-N // width)
-    return -(-tiles // cus) * width
+    return -(-tiles // cus) * (width + 64)
 
 
 def test_mlp_wide_tiles_ragged():
