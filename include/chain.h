@@ -281,10 +281,13 @@ chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg,
  *   dK,dV [B, Hkv, S, D] f32    (output)
  *   causal, scale  as given to chain_attn_fwd
  *   workspace  device buffer of at least chain_attn_bwd_workspace_bytes(B, Hq, S)
- *              bytes, 256-byte aligned; caller-owned scratch (holds D_i)
+ *              bytes, 256-byte aligned; caller-owned scratch (holds -D_i and
+ *              -LSE_i * log2(e) per row)
  * P is recomputed from Q, K and LSE, so LSE must be the one the forward
  * produced for these Q and K.  D must be 64 or 128.  Products are bf16 MFMAs
- * with f32 accumulation; P and dS are rounded to bf16 as MFMA operands.
+ * with f32 accumulation; the scores are formed from bf16 operands pre-scaled
+ * by scale * log2(e) (Q in the dQ kernel, as in the forward; K in the dK/dV
+ * kernel), and P and dS are rounded to bf16 as MFMA operands.
  * Every output element is written exactly once (no atomics), so repeated
  * calls give identical bits.  dQ, dK, dV and the workspace must not overlap
  * each other or any input (CHAIN_ERR_ALIAS).  Alignment: 16 bytes for all
