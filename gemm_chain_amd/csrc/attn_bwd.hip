@@ -10,25 +10,25 @@
 //   dQ = scale * dS.K,  dK = scale * dS^T.Q,  dV = P^T.dO,
 // dK and dV summed over the query heads that share a key/value head (GQA).
 //
-// Three kernels, no atomics (every output element is written once, so reruns
-// give identical bits):
-//  - rowdot: per query row, -D_i and -LSE_i * log2(e) into the workspace, in
-//    blocks of 16 rows [16 x -LSE*log2e | 16 x -D], rows padded to a multiple
-//    of 64 with (-inf, 0) so that padding rows get probability 0.  The scores
-//    are formed in base 2 from bf16 operands scaled by scale * log2(e) (Q in
-//    dq, as in the forward; K in dkdv); each S accumulator starts from
-//    -LSE * log2(e) (-inf where masked) and each dP accumulator from -D, so P
-//    is one exp2 and dS one product.
+// Two kernels, no atomics (every output element is written once, so reruns
+// give identical bits).  The scores are formed in base 2 from bf16 operands
+// scaled by scale * log2(e) (Q in dq, as in the forward; K in dkdv); each S
+// accumulator starts from -LSE * log2(e) (-inf where masked) and each dP
+// accumulator of dkdv from -D, so P is one exp2 and dS one product.
 //  - dq: eight waves (two per SIMD) take 32-row query blocks of WH heads of one
-//    key/value head and walk the visible 64-key tiles.  Per tile and wave:
+//    key/value head and walk the visible 64-key tiles.  Each wave first forms
+//    D_i = sum_d dO_id O_id for its rows and writes -LSE_i * log2(e) and -D_i
+//    to the workspace, in blocks of 16 rows [16 x -LSE*log2e | 16 x -D], rows
+//    padded to a multiple of 64 with (-inf, 0) so that padding rows get
+//    probability 0.  Per tile and wave:
 //    S^T = K.Q^T and dP^T = V.dO^T (Q and dO fragments stay in registers, each
 //    lane owns one query), dS^T = P^T * (dP^T - D) in registers, then
 //    dQ^T += K^T.dS^T with K^T read by ds_read_b64_tr_b16 in the key order the
 //    dS^T accumulator holds.
-//  - dkdv: four waves (one per SIMD, for the two 32-key accumulators) take 128
-//    keys of one key/value head, 32 per wave with their K and V fragments in
-//    registers, and walk every visible 64-row query tile of every query head of
-//    the group.  Per tile and wave, for its two 32-query halves: S = Q.K^T and
+//  - dkdv (launched after dq, whose workspace rows it reads): four waves (one
+//    per SIMD, for the two 32-key accumulators) take 128 keys of one key/value
+//    head, 32 per wave with their K and V fragments in registers, and walk every
+//    visible 64-row query tile of every query head of the group.  Per tile and wave, for its two 32-query halves: S = Q.K^T and
 //    dP = dO.V^T, P and dS, then dV^T += dO^T.P and dK^T += Q^T.dS with dO^T
 //    and Q^T read transposed.  With one wave per SIMD nothing else hides the
 //    softmax, so the wave interleaves it by hand: the second half's S/dP MFMAs
@@ -157,39 +157,6 @@ __device__ inline int padded_rows(int S) { return (S + kRowPad - 1) / kRowPad * 
 // Float index of row r's -LSE*log2e in its head's workspace block; -D_i is 16 further.
 __device__ inline int rv_index(int r) { return (r >> 4) * 32 + (r & 15); }
 
-// ---- D_i and LSE_i * log2(e) -------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void rowdot_kernel(const AttnBwdParams p) {
-  constexpr int CPR = D / 8, RPB = 256 / CPR;
-  const int Sp = padded_rows(p.S);
-  const int64_t rows = (int64_t)p.B * p.Hq * Sp;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
-  const int c = threadIdx.x % CPR;
-  const int s = (int)(row % Sp);
-  const int64_t bh = row / Sp;
-  const bool real = row < rows && s < p.S;
-  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-  float acc = 0.f;
-  if (real) {
-    const bf16x8 o = *(const bf16x8 *)((const __bf16 *)p.o + b * p.o_sb + h * p.o_sh + (int64_t)s * p.o_ss + 8 * c);
-    const bf16x8 g = *(const bf16x8 *)((const __bf16 *)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)s * p.do_ss + 8 * c);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf((float)o[j], (float)g[j], acc);
-  }
-#pragma unroll
-  for (int w = CPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, CPR);
-  if (row < rows && c == 0) {
-    float nl2 = -INFINITY;   // padding rows and rows without a visible key: probability 0
-    if (real) {
-      const float lse = p.lse[b * p.l_sb + h * p.l_sh + (int64_t)s * p.l_ss];
-      if (lse != -INFINITY) nl2 = -lse * kLog2e;
-    }
-    float *blk = p.rowv + bh * Sp * 2;
-    blk[rv_index(s)] = nl2;
-    blk[rv_index(s) + 16] = real ? -acc : 0.f;
-  }
-}
-
 // ---- dQ ----------------------------------------------------------------------
 template <int D, int WH>
 __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
@@ -249,9 +216,11 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
     const int wg_qmax = min(t * ROWS + ROWS, p.S) - 1;
 
     bf16x8 qf[KS], dof[KS];
+    float dsum = 0.f;   // this lane's half of D_i = sum_d dO_id O_id
     {
       const __bf16 *qr = (const __bf16 *)p.q + b * p.q_sb + head * p.q_sh + (int64_t)rr * p.q_ss + 8 * h2;
       const __bf16 *gr = (const __bf16 *)p.dout + b * p.do_sb + head * p.do_sh + (int64_t)rr * p.do_ss + 8 * h2;
+      const __bf16 *orr = (const __bf16 *)p.o + b * p.o_sb + head * p.o_sh + (int64_t)rr * p.o_ss + 8 * h2;
       // Q times scale * log2(e), rounded to bf16 (as the forward forms its scores)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -259,11 +228,25 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * c);
         dof[ks] = row_ok ? *(const bf16x8 *)(gr + 16 * ks) : bf16x8{};
+        const bf16x8 ov = row_ok ? *(const bf16x8 *)(orr + 16 * ks) : bf16x8{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsum = fmaf((float)ov[e], (float)dof[ks][e], dsum);
       }
     }
-    const float *rv = p.rowv + ((int64_t)b * p.Hq + head) * Sp * 2;
-    const float nl2 = row_ok ? rv[rv_index(rr)] : -INFINITY;
-    const float nd = row_ok ? rv[rv_index(rr) + 16] : 0.f;
+    // -LSE*log2(e) and -D_i of this lane's row (-inf and 0 past the last row or
+    // where no key is visible: probability 0); the dK/dV kernel, launched after
+    // this one, reads them from the workspace
+    float nl2 = -INFINITY;
+    if (row_ok) {
+      const float lse = p.lse[b * p.l_sb + head * p.l_sh + (int64_t)rr * p.l_ss];
+      if (lse != -INFINITY) nl2 = -lse * kLog2e;
+    }
+    const float nd = row_ok ? -(dsum + __shfl_xor(dsum, 32)) : 0.f;
+    if (h2 == 0 && my_row < Sp) {
+      float *rv = p.rowv + ((int64_t)b * p.Hq + head) * Sp * 2;
+      rv[rv_index(my_row)] = nl2;
+      rv[rv_index(my_row) + 16] = nd;
+    }
     // the S accumulators start from -LSE * log2(e) of the lane's query (a -D
     // start for dP as well would cost 16 more registers than the kernel has)
     f32x16 sinit;
@@ -587,10 +570,6 @@ CHAIN_BWD_KERNELS(128)
 
 template <int D>
 hipError_t launch_d(const AttnBwdParams &p, hipStream_t s) {
-  const int64_t Sp = (p.S + kRowPad - 1) / kRowPad * kRowPad;
-  const int64_t rows = (int64_t)p.B * p.Hq * Sp;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   const int group = p.Hq / p.Hkv;
   const int wh = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
   const int rows_t = 32 * (8 / wh);

@@ -174,7 +174,7 @@ struct AttnBwdParams {
   const float *lse;                   // natural log, [B, Hq, S]
   float *dq, *dk, *dv;                // outputs, f32
   float *rowv;                        // workspace: per (b, h), rows padded to a multiple of 64,
-                                      // blocks of 16 rows [16 x LSE*log2(e) | 16 x D_i]
+                                      // blocks of 16 rows [16 x -LSE*log2(e) | 16 x -D_i]
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
