@@ -214,7 +214,9 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     // ---- tile iterators (uniform over the workgroup).  Tiles of BN keys are
     // cut inside each key range, up to the last key position this tile's
     // queries can see (stop); n counts them.  Stepping within a range is one
-    // add and one compare; the range switch is rare.
+    // add and one compare; the range switch is rare.  Scalar branches cost tens
+    // of cycles even when not taken, so the three iterators of the loop step
+    // together behind one branch.
     struct It { int ri, k0, stop, kend, off; };   // ri == p.kr.n: past the last tile
     auto range_stop = [&](int r) {
       return p.causal ? min(p.kr.end[r], wg_qmax - p.kr.pos_off[r] + 1) : p.kr.end[r];
@@ -224,11 +226,21 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         const int st = range_stop(r);
         if (st > p.kr.beg[r]) return It{r, p.kr.beg[r], st, p.kr.end[r], p.kr.pos_off[r]};
       }
-      return It{p.kr.n, 0, 0, 0, 0};
+      return It{p.kr.n, 0, INT_MAX, 0, 0};   // never steps into a range switch
     };
     auto step = [&](It &x) {
       x.k0 += BN;
       if (x.k0 >= x.stop) x = seek(x.ri + 1);
+    };
+    auto step3 = [&](It &a, It &b, It &c) {
+      a.k0 += BN;
+      b.k0 += BN;
+      c.k0 += BN;
+      if ((a.k0 >= a.stop) | (b.k0 >= b.stop) | (c.k0 >= c.stop)) {
+        if (a.k0 >= a.stop) a = seek(a.ri + 1);
+        if (b.k0 >= b.stop) b = seek(b.ri + 1);
+        if (c.k0 >= c.stop) c = seek(c.ri + 1);
+      }
     };
     auto valid = [&](const It &x) { return x.ri < p.kr.n; };
     int n = 0;
@@ -238,9 +250,9 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     }
     // What this wave does with a tile: skip it, take it whole, or mask it.
     auto tile_class = [&](const It &x) -> int {
-      if (!valid(x) || !wave_rows) return TILE_SKIP;
       const int nvalid = min(BN, x.kend - x.k0);
-      return classify_tile(p.causal, w_qmin, w_qmax, x.k0 + x.off, x.k0 + nvalid - 1 + x.off, nvalid < BN);
+      const int c = classify_tile(p.causal, w_qmin, w_qmax, x.k0 + x.off, x.k0 + nvalid - 1 + x.off, nvalid < BN);
+      return (valid(x) & wave_rows) ? c : TILE_SKIP;
     };
     // Direct-to-LDS loads of one operand of one tile into a ring stage: each
     // wave-level load puts 64 lanes x 16 bytes (RPL key rows) into LDS.  The
@@ -324,20 +336,17 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       // lane sum of at most 2^kTau proves no term is, so the max is computed
       // (and the rule below applied) only when some lane sum exceeds it, or
       // before the first reference exists.
+      // (Before the first reference exists the fast path's values are discarded.)
       float rs = 0.f;
-      bool slow = !ref_ready;
-      if (!slow) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[kb][r]);
-            rs += e;
-            pk[kb][r >> 3][r & 7] = (__bf16)e;
-          }
-        slow = __any(!(rs <= kLaneSumMax));
-      }
-      if (slow) {
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s[kb][r]);
+          rs += e;
+          pk[kb][r >> 3][r & 7] = (__bf16)e;
+        }
+      if (__any(!(rs <= kLaneSumMax)) | !ref_ready) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -392,9 +401,9 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     // tile j, so every step has the same loads in flight.  Per wave the load
     // groups (LPW loads each) are issued in the order K0 V0 K1 V1 K2 | K3 V2 |
     // K4 V3 | ..., and a tile's K and V must have landed before the barrier
-    // ahead of the phase that first reads them: group 0 waits at the end of
-    // each S step for all but its last 4 groups, group 1 at the end of each C
-    // step for all but its last 2.
+    // ahead of the phase that first reads them: every wave waits at the end of
+    // each C step for all but its last 2 groups (C_j: K of tile j+1 and V of
+    // tile j, issued in S_(j-2), three phases earlier).
     if (n > 0) {
       // cur: tile j (K.Q^T, softmax); itv: tile j+2 and itk: tile j+3, whose V
       // and K are loaded in S_j.  Past the last tile the loads repeat the first
@@ -425,10 +434,8 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         if (cls != TILE_SKIP) mfma_run(QK{}, NONE{}, ks, vs, [](int) {});
         if (prev_live) mfma_run(NONE{}, PV{}, ks, vs, [](int) {});
         __builtin_amdgcn_s_setprio(0);
-        if (grp == 1) {
-          wait_vmcnt<2 * LPW>();
-          zero_v_tail(cur, vring + ST * TB);
-        }
+        wait_vmcnt<2 * LPW>();
+        zero_v_tail(cur, vring + ST * TB);
       };
       // S_j: this wave's part of tile j+3's K and tile j+2's V goes out first,
       // so that the loads are in flight during the softmax
@@ -437,14 +444,8 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + ((ST + 3) % NST) * TB);
         issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + ((ST + 2) % NST) * TB);
         if (cls != TILE_SKIP) softmax(cur, cls);
-        if (grp == 0) {
-          wait_vmcnt<4 * LPW>();
-          zero_v_tail(cur, vring + ST * TB);
-        }
         prev_live = cls != TILE_SKIP;
-        step(cur);
-        step(itv);
-        step(itk);
+        step3(cur, itv, itk);
         cls = tile_class(cur);
       };
       using St0 = std::integral_constant<int, 0>;

@@ -45,12 +45,12 @@ enum TileClass : int { TILE_SKIP = 0, TILE_FULL = 1, TILE_DIAG = 2 };
 
 // Query rows with positions in [qmin, qmax] against a key tile with positions
 // [kmin, kmax]; `ragged` marks a key tile cut short by its range end.
+// Written with selects only: on the GPU this runs once per tile in the loop.
 __host__ __device__ inline int classify_tile(int causal, int32_t qmin, int32_t qmax,
                                              int32_t kmin, int32_t kmax, bool ragged) {
-  if (causal && kmin > qmax) return TILE_SKIP;
-  if (ragged) return TILE_DIAG;
-  if (!causal || kmax <= qmin) return TILE_FULL;
-  return TILE_DIAG;
+  const bool skip = (causal != 0) & (kmin > qmax);
+  const bool diag = ragged | ((causal != 0) & (kmax > qmin));
+  return skip ? TILE_SKIP : diag ? TILE_DIAG : TILE_FULL;
 }
 
 // Block ids are dealt to the XCDs round-robin (id % 8).  Map them so that XCD x
