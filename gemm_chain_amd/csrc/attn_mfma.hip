@@ -169,36 +169,146 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     const int xv = D == 128 ? (trow & 3) : ((trow >> 1) & 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) voff[db] = trow * RB + ((4 * (db ^ xv) + ylane) << 4) + 8 * (lane & 1);
+    // Hide the offsets' known bits: otherwise the compiler may turn offset +
+    // stage constant into an OR per read instead of one add and immediate offsets.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(voff[db]));
   }
 
-  for (int pass = 0; pass < 2; ++pass) {
-    const int t = pass == 0 ? pr : T - 1 - pr;
-    if (pass == 1 && t == pr) break;
+  // ---- the two passes of an item (query tiles pr and T-1-pr) share one body
+  // and the state below, which set_pass fills for query tile t.  Pass 1's Q
+  // rows and first tiles are fetched before pass 0's outputs are stored, so
+  // they do not queue behind the stores.
+  int wg_qmax = 0, row0 = 0, my_row = 0, n = 0;
+  int32_t w_qmin = 0, w_qmax = 0, my_qpos = 0;
+  bool wave_rows = false, row_ok = false;
+  bf16x8 qraw[KS], qf[KS];
+
+  // ---- tile iterators (uniform over the workgroup).  Tiles of BN keys are
+  // cut inside each key range, up to the last key position this tile's
+  // queries can see (stop); n counts them.  Stepping within a range is one
+  // add and one compare; the range switch is rare.  Scalar branches cost tens
+  // of cycles even when not taken, so the three iterators of the loop step
+  // together behind one branch.
+  struct It { int ri, k0, stop, kend, off; };   // ri == p.kr.n: past the last tile
+  auto range_stop = [&](int r) {
+    return p.causal ? min(p.kr.end[r], wg_qmax - p.kr.pos_off[r] + 1) : p.kr.end[r];
+  };
+  auto seek = [&](int r) -> It {   // first tile of the first live range at or after r
+    for (; r < p.kr.n; ++r) {
+      const int st = range_stop(r);
+      if (st > p.kr.beg[r]) return It{r, p.kr.beg[r], st, p.kr.end[r], p.kr.pos_off[r]};
+    }
+    return It{p.kr.n, 0, INT_MAX, 0, 0};   // never steps into a range switch
+  };
+  auto step = [&](It &x) {
+    x.k0 += BN;
+    if (x.k0 >= x.stop) x = seek(x.ri + 1);
+  };
+  auto step3 = [&](It &a, It &b, It &c) {
+    a.k0 += BN;
+    b.k0 += BN;
+    c.k0 += BN;
+    if ((a.k0 >= a.stop) | (b.k0 >= b.stop) | (c.k0 >= c.stop)) {
+      if (a.k0 >= a.stop) a = seek(a.ri + 1);
+      if (b.k0 >= b.stop) b = seek(b.ri + 1);
+      if (c.k0 >= c.stop) c = seek(c.ri + 1);
+    }
+  };
+  auto valid = [&](const It &x) { return x.ri < p.kr.n; };
+  // What this wave does with a tile: skip it, take it whole, or mask it.
+  auto tile_class = [&](const It &x) -> int {
+    const int nvalid = min(BN, x.kend - x.k0);
+    const int c = classify_tile(p.causal, w_qmin, w_qmax, x.k0 + x.off, x.k0 + nvalid - 1 + x.off, nvalid < BN);
+    return (valid(x) & wave_rows) ? c : TILE_SKIP;
+  };
+  // Direct-to-LDS loads of one operand of one tile into a ring stage: each
+  // wave-level load puts 64 lanes x 16 bytes (RPL key rows) into LDS.  The
+  // buffer descriptor starts at the tile's first key row and ends at its
+  // range end, so the same branch-free loads serve whole tiles and tiles cut
+  // short: keys past the range end are out of the buffer and read as zero
+  // (their scores are masked, their V rows cleared as well).
+  auto issue = [&](const char *base, uint32_t ss2, const int *lo, const It &x, char *stage) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(base + (uint32_t)x.k0 * ss2), 0, (int)((uint32_t)(x.kend - x.k0 - 1) * ss2 + 2 * D), 0x00020000);
+#pragma unroll
+    for (int q = 0; q < LPW; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(stage + (wave * LPW + q) * 1024),
+                                               16, lo[q], 0, 0, 0);
+  };
+  // V rows past a range end are cleared once this wave's own loads of them
+  // have landed, so that a masked key multiplies zeros whatever the input holds.
+  auto zero_v_tail = [&](const It &x, char *stage) {
+    if (valid(x) && x.k0 + BN > x.kend) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < LPW; ++q)
+        if (x.k0 + lrow[q] >= x.kend) *(u32x4 *)(stage + (wave * LPW + q) * 1024 + lane * 16) = z;
+      wait_lgkmcnt0();
+    }
+  };
+  It first{}, cur{}, itv{}, itk{};
+
+  auto set_pass = [&](int t) {
     const int wg_row0 = t * ROWS;
     const int wg_last = min(wg_row0 + ROWS, p.Sq) - 1;
-    const int32_t wg_qmax = row_position(p.qruns, wg_last);
-    const int row0 = wg_row0 + qblk * 32;
-    const bool wave_rows = row0 < p.Sq;
+    wg_qmax = row_position(p.qruns, wg_last);
+    row0 = wg_row0 + qblk * 32;
+    wave_rows = row0 < p.Sq;
     const int w_last = min(row0 + 31, p.Sq - 1);
-    const int32_t w_qmin = row_position(p.qruns, min(row0, p.Sq - 1));
-    const int32_t w_qmax = row_position(p.qruns, w_last);
-    const int my_row = row0 + l32;
-    const bool row_ok = my_row < p.Sq;
-    const int32_t my_qpos = row_position(p.qruns, min(my_row, p.Sq - 1));
-
-    bf16x8 qf[KS];
-    {
-      const __bf16 *qrow = (const __bf16 *)p.q + b * p.q_sb + head * p.q_sh +
-                           (int64_t)min(my_row, p.Sq - 1) * p.q_ss + 8 * h2;
-      // Q times scale * log2(e), rounded to bf16: the products then come out of
-      // the MFMA in base-2 units.
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 raw = *(const bf16x8 *)(qrow + ks * 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = row_ok ? (__bf16)((float)raw[e] * c) : (__bf16)0.f;
-      }
+    w_qmin = row_position(p.qruns, min(row0, p.Sq - 1));
+    w_qmax = row_position(p.qruns, w_last);
+    my_row = row0 + l32;
+    row_ok = my_row < p.Sq;
+    my_qpos = row_position(p.qruns, min(my_row, p.Sq - 1));
+    n = 0;
+    for (int r = 0; r < p.kr.n; ++r) {
+      const int st = range_stop(r);
+      if (st > p.kr.beg[r]) n += (st - p.kr.beg[r] + BN - 1) / BN;
     }
+  };
+  // The pass's Q rows; convert_q then forms Q times scale * log2(e), rounded
+  // to bf16, so the products come out of the MFMA in base-2 units.
+  auto load_q = [&] {
+    const __bf16 *qrow = (const __bf16 *)p.q + b * p.q_sb + head * p.q_sh +
+                         (int64_t)min(my_row, p.Sq - 1) * p.q_ss + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *(const bf16x8 *)(qrow + ks * 16);
+  };
+  auto convert_q = [&] {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = row_ok ? (__bf16)((float)qraw[ks][e] * c) : (__bf16)0.f;
+  };
+  // The ring's first loads of a pass: K0 V0 K1 V1 K2.  cur: tile j (K.Q^T,
+  // softmax); itv: tile j+2 and itk: tile j+3, whose V and K are loaded in S_j.
+  // Past the last tile the loads repeat the first tile into the free stages, so
+  // every step has the same loads in flight.
+  auto start_tiles = [&] {
+    if (n > 0) {
+      first = seek(0);
+      cur = first;
+      itv = first;
+      step(itv);
+      issue(kb8, kss2, klo, cur, kring);
+      issue(vb8, vss2, vlo, cur, vring);
+      issue(kb8, kss2, klo, valid(itv) ? itv : first, kring + TB);
+      issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + TB);
+      step(itv);
+      itk = itv;
+      issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + 2 * TB);
+      step(itk);
+    }
+  };
+
+  const bool two = T - 1 - pr != pr;   // the middle tile of an odd count is one pass
+  set_pass(pr);
+  load_q();
+  start_tiles();
+  convert_q();
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1 && !two) break;
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -211,74 +321,6 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     f32x16 s[2];
     bf16x8 pk[2][2];
 
-    // ---- tile iterators (uniform over the workgroup).  Tiles of BN keys are
-    // cut inside each key range, up to the last key position this tile's
-    // queries can see (stop); n counts them.  Stepping within a range is one
-    // add and one compare; the range switch is rare.  Scalar branches cost tens
-    // of cycles even when not taken, so the three iterators of the loop step
-    // together behind one branch.
-    struct It { int ri, k0, stop, kend, off; };   // ri == p.kr.n: past the last tile
-    auto range_stop = [&](int r) {
-      return p.causal ? min(p.kr.end[r], wg_qmax - p.kr.pos_off[r] + 1) : p.kr.end[r];
-    };
-    auto seek = [&](int r) -> It {   // first tile of the first live range at or after r
-      for (; r < p.kr.n; ++r) {
-        const int st = range_stop(r);
-        if (st > p.kr.beg[r]) return It{r, p.kr.beg[r], st, p.kr.end[r], p.kr.pos_off[r]};
-      }
-      return It{p.kr.n, 0, INT_MAX, 0, 0};   // never steps into a range switch
-    };
-    auto step = [&](It &x) {
-      x.k0 += BN;
-      if (x.k0 >= x.stop) x = seek(x.ri + 1);
-    };
-    auto step3 = [&](It &a, It &b, It &c) {
-      a.k0 += BN;
-      b.k0 += BN;
-      c.k0 += BN;
-      if ((a.k0 >= a.stop) | (b.k0 >= b.stop) | (c.k0 >= c.stop)) {
-        if (a.k0 >= a.stop) a = seek(a.ri + 1);
-        if (b.k0 >= b.stop) b = seek(b.ri + 1);
-        if (c.k0 >= c.stop) c = seek(c.ri + 1);
-      }
-    };
-    auto valid = [&](const It &x) { return x.ri < p.kr.n; };
-    int n = 0;
-    for (int r = 0; r < p.kr.n; ++r) {
-      const int st = range_stop(r);
-      if (st > p.kr.beg[r]) n += (st - p.kr.beg[r] + BN - 1) / BN;
-    }
-    // What this wave does with a tile: skip it, take it whole, or mask it.
-    auto tile_class = [&](const It &x) -> int {
-      const int nvalid = min(BN, x.kend - x.k0);
-      const int c = classify_tile(p.causal, w_qmin, w_qmax, x.k0 + x.off, x.k0 + nvalid - 1 + x.off, nvalid < BN);
-      return (valid(x) & wave_rows) ? c : TILE_SKIP;
-    };
-    // Direct-to-LDS loads of one operand of one tile into a ring stage: each
-    // wave-level load puts 64 lanes x 16 bytes (RPL key rows) into LDS.  The
-    // buffer descriptor starts at the tile's first key row and ends at its
-    // range end, so the same branch-free loads serve whole tiles and tiles cut
-    // short: keys past the range end are out of the buffer and read as zero
-    // (their scores are masked, their V rows cleared as well).
-    auto issue = [&](const char *base, uint32_t ss2, const int *lo, const It &x, char *stage) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(base + (uint32_t)x.k0 * ss2), 0, (int)((uint32_t)(x.kend - x.k0 - 1) * ss2 + 2 * D), 0x00020000);
-#pragma unroll
-      for (int q = 0; q < LPW; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(stage + (wave * LPW + q) * 1024),
-                                                 16, lo[q], 0, 0, 0);
-    };
-    // V rows past a range end are cleared once this wave's own loads of them
-    // have landed, so that a masked key multiplies zeros whatever the input holds.
-    auto zero_v_tail = [&](const It &x, char *stage) {
-      if (valid(x) && x.k0 + BN > x.kend) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int q = 0; q < LPW; ++q)
-          if (x.k0 + lrow[q] >= x.kend) *(u32x4 *)(stage + (wave * LPW + q) * 1024 + lane * 16) = z;
-        wait_lgkmcnt0();
-      }
-    };
     // MFMA phase: NQ products of S^T = K.Q^T on a K stage, then NP products
     // of O^T += V^T.P^T on a V stage (the previous tile's P).  LDS fragments
     // are read kAhead MFMAs ahead of use, across the boundary of the two runs.
@@ -405,21 +447,9 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     // each C step for all but its last 2 groups (C_j: K of tile j+1 and V of
     // tile j, issued in S_(j-2), three phases earlier).
     if (n > 0) {
-      // cur: tile j (K.Q^T, softmax); itv: tile j+2 and itk: tile j+3, whose V
-      // and K are loaded in S_j.  Past the last tile the loads repeat the first
-      // tile into the free stages, so every step has the same loads in flight.
-      const It first = seek(0);
-      It cur = first, itv = first, itk = first;
-      step(itv);
-      issue(kb8, kss2, klo, cur, kring);
-      issue(vb8, vss2, vlo, cur, vring);
-      issue(kb8, kss2, klo, valid(itv) ? itv : first, kring + TB);
-      issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + TB);
-      step(itv);
-      itk = itv;
-      issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + 2 * TB);
-      step(itk);
-      wait_vmcnt<4 * LPW>();   // K of tile 0 has landed
+      // K of tile 0 has landed (pass 1: all its first loads landed before the
+      // previous pass's outputs were stored, and the stores must not be waited on)
+      if (pass == 0) wait_vmcnt<4 * LPW>();
       barrier();
       int cls = tile_class(cur);
       bool prev_live = false;
@@ -481,11 +511,21 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     wait_vmcnt<0>();   // no load into LDS may outlive the pass
     __builtin_amdgcn_s_barrier();
 
-    // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
+    // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l), after pass 1's Q
+    // rows and first tiles are in
+    const int e_row = my_row;
+    const bool e_ok = row_ok;
+    if (pass == 0 && two) {
+      set_pass(T - 1 - pr);
+      load_q();
+      start_tiles();
+      wait_vmcnt<0>();
+      convert_q();
+    }
     const float lt = pair_sum(l);
-    if (row_ok) {
+    if (e_ok) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int64_t orow = b * p.o_sb + head * p.o_sh + (int64_t)my_row * p.o_ss;
+      const int64_t orow = b * p.o_sb + head * p.o_sh + (int64_t)e_row * p.o_ss;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -502,7 +542,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
           }
         }
       if (h2 == 0)
-        p.lse[b * p.l_sb + head * p.l_sh + (int64_t)my_row * p.l_ss] =
+        p.lse[b * p.l_sb + head * p.l_sh + (int64_t)e_row * p.l_ss] =
             lt > 0.f ? (m + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
