@@ -145,18 +145,19 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   // swizzle costs nothing there.
   auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
   auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
-  int lrow[LPW], kch[LPW], vch[LPW];
+  // Each group of four waves loads one operand of every tile: group 0 all of
+  // K, group 1 all of V (LO loads of 1 KB per wave and tile).  lo: per-lane byte
+  // offsets of a whole tile's loads from its first key.
+  constexpr int LO = 2 * LPW;
+  const int w4 = wave & 3;
+  const char *const own_b8 = grp == 0 ? kb8 : vb8;
+  const uint32_t own_ss2 = grp == 0 ? kss2 : vss2;
+  int lrow[LO], ldo[LO];
 #pragma unroll
-  for (int q = 0; q < LPW; ++q) {
-    lrow[q] = (wave * LPW + q) * RPL + lane / CPR;
-    kch[q] = (lane % CPR) ^ kswz(lrow[q]);
-    vch[q] = (lane % CPR) ^ vswz(lrow[q]);
-  }
-  int klo[LPW], vlo[LPW];   // per-lane byte offsets of a whole tile's loads from its first key
-#pragma unroll
-  for (int q = 0; q < LPW; ++q) {
-    klo[q] = lrow[q] * kss2 + 16 * kch[q];
-    vlo[q] = lrow[q] * vss2 + 16 * vch[q];
+  for (int q = 0; q < LO; ++q) {
+    lrow[q] = (w4 * LO + q) * RPL + lane / CPR;
+    const int ch = (lane % CPR) ^ (grp == 0 ? kswz(lrow[q]) : vswz(lrow[q]));
+    ldo[q] = lrow[q] * own_ss2 + 16 * ch;
   }
   // Per-lane byte offsets of the MFMA fragments within a K or a V stage.
   int koff[KS], voff[DB];
@@ -228,22 +229,23 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   // range end, so the same branch-free loads serve whole tiles and tiles cut
   // short: keys past the range end are out of the buffer and read as zero
   // (their scores are masked, their V rows cleared as well).
-  auto issue = [&](const char *base, uint32_t ss2, const int *lo, const It &x, char *stage) {
+  auto issue = [&](const It &x, char *stage) {   // this wave's part of its group's operand
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(base + (uint32_t)x.k0 * ss2), 0, (int)((uint32_t)(x.kend - x.k0 - 1) * ss2 + 2 * D), 0x00020000);
+        (void *)(own_b8 + (uint32_t)x.k0 * own_ss2), 0, (int)((uint32_t)(x.kend - x.k0 - 1) * own_ss2 + 2 * D),
+        0x00020000);
 #pragma unroll
-    for (int q = 0; q < LPW; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(stage + (wave * LPW + q) * 1024),
-                                               16, lo[q], 0, 0, 0);
+    for (int q = 0; q < LO; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(stage + (w4 * LO + q) * 1024),
+                                               16, ldo[q], 0, 0, 0);
   };
   // V rows past a range end are cleared once this wave's own loads of them
   // have landed, so that a masked key multiplies zeros whatever the input holds.
   auto zero_v_tail = [&](const It &x, char *stage) {
-    if (valid(x) && x.k0 + BN > x.kend) {
+    if ((grp == 1) & valid(x) & (x.k0 + BN > x.kend)) {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int q = 0; q < LPW; ++q)
-        if (x.k0 + lrow[q] >= x.kend) *(u32x4 *)(stage + (wave * LPW + q) * 1024 + lane * 16) = z;
+      for (int q = 0; q < LO; ++q)
+        if (x.k0 + lrow[q] >= x.kend) *(u32x4 *)(stage + (w4 * LO + q) * 1024 + lane * 16) = z;
       wait_lgkmcnt0();
     }
   };
@@ -281,23 +283,23 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[ks][e] = row_ok ? (__bf16)((float)qraw[ks][e] * c) : (__bf16)0.f;
   };
-  // The ring's first loads of a pass: K0 V0 K1 V1 K2.  cur: tile j (K.Q^T,
-  // softmax); itv: tile j+2 and itk: tile j+3, whose V and K are loaded in S_j.
-  // Past the last tile the loads repeat the first tile into the free stages, so
-  // every step has the same loads in flight.
+  // The ring's first loads of a pass: group 0 K of tiles 0, 1 and 2, group 1
+  // V of tiles 0 and 1.  cur: tile j (K.Q^T, softmax); itv: tile j+2 and itk:
+  // tile j+3, whose V and K are loaded in S_j.  Past the last tile the loads
+  // repeat the first tile into the free stages, so every step has the same
+  // loads in flight.
+  char *const own_ring = grp == 0 ? kring : vring;
   auto start_tiles = [&] {
     if (n > 0) {
       first = seek(0);
       cur = first;
       itv = first;
       step(itv);
-      issue(kb8, kss2, klo, cur, kring);
-      issue(vb8, vss2, vlo, cur, vring);
-      issue(kb8, kss2, klo, valid(itv) ? itv : first, kring + TB);
-      issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + TB);
+      issue(cur, own_ring);
+      issue(valid(itv) ? itv : first, own_ring + TB);
       step(itv);
       itk = itv;
-      issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + 2 * TB);
+      if (grp == 0) issue(valid(itk) ? itk : first, kring + 2 * TB);
       step(itk);
     }
   };
@@ -324,10 +326,23 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     // MFMA phase: NQ products of S^T = K.Q^T on a K stage, then NP products
     // of O^T += V^T.P^T on a V stage (the previous tile's P).  LDS fragments
     // are read kAhead MFMAs ahead of use, across the boundary of the two runs.
-    auto mfma_run = [&](auto nq_c, auto np_c, const char *ks, const char *vs, auto hook) {
+    // The first kAhead K fragments of a K.Q^T run (pre = true) come from fq,
+    // read at the end of the softmax step before it, so their LDS latency passes
+    // under the barrier.
+    bf16x8 fq[kAhead];
+    auto kfrag = [&](const char *ks, int i) -> bf16x8 {
+      return *(const bf16x8 *)(ks + koff[i >> 1] + (i & 1) * 32 * RB);
+    };
+    auto early = [&](const char *ks) {
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) fq[i] = kfrag(ks, i);
+    };
+    auto mfma_run = [&](auto nq_c, auto np_c, const char *ks, const char *vs, auto pre_c, auto hook) {
       constexpr int NQ = decltype(nq_c)::value, NP = decltype(np_c)::value, N = NQ + NP;
+      constexpr bool PRE = decltype(pre_c)::value;
+      static_assert(!PRE || NQ >= kAhead, "preloaded fragments are K fragments");
       auto frag = [&](int i) -> bf16x8 {
-        if (i < NQ) return *(const bf16x8 *)(ks + koff[i >> 1] + (i & 1) * 32 * RB);
+        if (i < NQ) return kfrag(ks, i);
         const int k = i - NQ;
         const __bf16 *a = (const __bf16 *)(vs + voff[k >> 2] + (((k >> 1) & 1) * 32 + 16 * (k & 1)) * RB);
         const i16x4 lo = ds_read_tr(a), hi = ds_read_tr(a + 8 * D);
@@ -336,7 +351,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       bf16x8 f[kAhead];
 #pragma unroll
       for (int i = 0; i < kAhead; ++i)
-        if (i < N) f[i] = frag(i);
+        if (i < N) f[i] = PRE ? fq[i] : frag(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < N; ++i) {
@@ -436,21 +451,24 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     // MFMA run meets the other wave's softmax.  In phase ph group 0 runs step
     // ph and group 1 step ph-1 of that sequence (C_j is step 2j, S_j step 2j+1).
     //
-    // Tile j's K sits in K stage j%4 and is read in phases 2j and 2j+1; its V
-    // sits in V stage j%4 and is read in phases 2j+2 and 2j+3.  S_j issues K of
-    // tile j+3 and V of tile j+2 (phase 2j+1 or 2j+2), whose stages were last
-    // read in phase 2j-1.  Past the last tile the free stages are refilled with
-    // tile j, so every step has the same loads in flight.  Per wave the load
-    // groups (LPW loads each) are issued in the order K0 V0 K1 V1 K2 | K3 V2 |
-    // K4 V3 | ..., and a tile's K and V must have landed before the barrier
-    // ahead of the phase that first reads them: every wave waits at the end of
-    // each C step for all but its last 2 groups (C_j: K of tile j+1 and V of
-    // tile j, issued in S_(j-2), three phases earlier).
+    // Tile j's K sits in K stage j%4 and is read in phases 2j and 2j+1 (its
+    // first fragments at the end of phases 2j-1 and 2j); its V sits in V stage
+    // j%4 and is read in phases 2j+2 and 2j+3.  In S_j group 0 issues all of
+    // tile j+3's K (phase 2j+1) and group 1 all of tile j+2's V (phase 2j+2),
+    // into stages last read in phase 2j-1.  Past the last tile the free stages
+    // are refilled with tile j, so every step has the same loads in flight.
+    // Each wave issues LO loads per S step (group 0: K0 K1 K2 | K3 | K4 | ...,
+    // group 1: V0 V1 | V2 | V3 | ...) and waits at the end of each C step for
+    // all but those of its latest S step: at the end of C_j (phase 2j for group
+    // 0, 2j+1 for group 1) K of tile j+1, resp. V of tile j, has landed, issued
+    // three phases earlier, and the barrier that follows publishes it before the
+    // first fragment reads of C_j+1.
     if (n > 0) {
       // K of tile 0 has landed (pass 1: all its first loads landed before the
       // previous pass's outputs were stored, and the stores must not be waited on)
-      if (pass == 0) wait_vmcnt<4 * LPW>();
+      if (pass == 0) wait_vmcnt<2 * LO>();   // group 0: K of tile 0 (group 1: no wait)
       barrier();
+      early(kring);
       int cls = tile_class(cur);
       bool prev_live = false;
       // C_j: the K.Q^T run of tile j (in K stage j%4), then the P.V run of tile
@@ -461,22 +479,24 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         const char *ks = kring + ST * TB;
         const char *vs = vring + ((ST + NST - 1) % NST) * TB;
         __builtin_amdgcn_s_setprio(1);
-        if (cls != TILE_SKIP) mfma_run(QK{}, NONE{}, ks, vs, [](int) {});
-        if (prev_live) mfma_run(NONE{}, PV{}, ks, vs, [](int) {});
+        if (cls != TILE_SKIP) mfma_run(QK{}, NONE{}, ks, vs, std::true_type{}, [](int) {});
+        if (prev_live) mfma_run(NONE{}, PV{}, ks, vs, std::false_type{}, [](int) {});
         __builtin_amdgcn_s_setprio(0);
-        wait_vmcnt<2 * LPW>();
+        wait_vmcnt<LO>();   // all but the loads of this wave's latest S step
         zero_v_tail(cur, vring + ST * TB);
       };
-      // S_j: this wave's part of tile j+3's K and tile j+2's V goes out first,
-      // so that the loads are in flight during the softmax
+      // S_j: this wave's part of tile j+3's K (group 0) or tile j+2's V (group 1)
+      // goes out first, so that the loads are in flight during the softmax; at
+      // the end, the first K fragments of C_j+1
       auto softmax_step = [&](auto st_c) {
         constexpr int ST = decltype(st_c)::value;
-        issue(kb8, kss2, klo, valid(itk) ? itk : first, kring + ((ST + 3) % NST) * TB);
-        issue(vb8, vss2, vlo, valid(itv) ? itv : first, vring + ((ST + 2) % NST) * TB);
+        const It &ld = grp == 0 ? (valid(itk) ? itk : first) : (valid(itv) ? itv : first);
+        issue(ld, grp == 0 ? kring + ((ST + 3) % NST) * TB : vring + ((ST + 2) % NST) * TB);
         if (cls != TILE_SKIP) softmax(cur, cls);
         prev_live = cls != TILE_SKIP;
         step3(cur, itv, itk);
         cls = tile_class(cur);
+        early(kring + ((ST + 1) % NST) * TB);
       };
       using St0 = std::integral_constant<int, 0>;
       using St1 = std::integral_constant<int, 1>;
