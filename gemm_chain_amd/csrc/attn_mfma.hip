@@ -25,12 +25,14 @@
 // phases, so on each SIMD one wave's MFMA run meets the other wave's softmax.
 // Tiles reach LDS by buffer loads that write LDS directly (64 lanes x 16 bytes
 // per wave-level load, no staging registers, no LDS write instructions) into a
-// K ring and a V ring of four stages each, tile j+3's K and tile j+2's V issued
-// at the start of softmax phase j.  Staged rows are not padded: 16-byte chunks
-// are XOR-swizzled per row so that the 16-byte K fragment reads and the
-// transposing V reads each hit distinct bank groups.  Inside each MFMA run the
-// LDS fragments are read kAhead MFMAs ahead of use (pinned with scheduling
-// barriers).
+// K ring and a V ring of four stages each: at the start of softmax phase j,
+// waves 0-3 issue all of tile j+3's K and waves 4-7 all of tile j+2's V.
+// Staged rows are not padded: 16-byte chunks are XOR-swizzled per row so that
+// the 16-byte K fragment reads and the transposing V reads each hit distinct
+// bank groups.  Inside each MFMA run the LDS fragments are read kAhead MFMAs
+// ahead of use (pinned with scheduling barriers); the first ones of a K.Q^T run
+// are read at the end of the softmax phase before it.  Scalar branches cost
+// tens of cycles even when not taken, so the tile loop keeps them few.
 //
 // Q is multiplied by scale * log2(e) and rounded to bf16 once per query tile,
 // and each K.Q^T accumulator starts from minus the row's reference max m, so
