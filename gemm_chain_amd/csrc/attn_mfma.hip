@@ -325,9 +325,10 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     f32x16 s[2];
     bf16x8 pk[2][2];
 
-    // MFMA phase: NQ products of S^T = K.Q^T on a K stage, then NP products
-    // of O^T += V^T.P^T on a V stage (the previous tile's P).  LDS fragments
-    // are read kAhead MFMAs ahead of use, across the boundary of the two runs.
+    // MFMA run: NQ products of S^T = K.Q^T on a K stage, then NP products of
+    // O^T += V^T.P^T on a V stage (the previous tile's P).  LDS fragments are
+    // read kAhead MFMAs ahead of use; a K.Q^T run may take its first ones from
+    // fq (pre).
     // The first kAhead K fragments of a K.Q^T run (pre = true) come from fq,
     // read at the end of the softmax step before it, so their LDS latency passes
     // under the barrier.
