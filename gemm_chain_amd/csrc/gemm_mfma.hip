@@ -51,7 +51,13 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = 128, TN = 128, TK = 32;   // f32 path
 
-__device__ inline i16x4 ds_read_tr(const __bf16 *p) {
+// Transposing LDS read (in each group of 16 lanes, lane i receives element i % 4
+// of the 4-element rows addressed by lanes 4e + i / 4, e = 0..3).  The restrict
+// qualifier gives the inlined read alias-scope information; without it the
+// compiler cannot tell it from direct-to-LDS loads in flight and waits for all
+// of them (vmcnt(0)) before it.  Every stage a read touches has landed and
+// passed a barrier.
+__device__ inline i16x4 ds_read_tr(const __bf16 *__restrict__ p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
@@ -801,9 +807,16 @@ CHAIN_W8_KERNELS(silu, CHAIN_ACT_SILU)
 // before its end, after the last read of the stage and before the reads of the
 // next.  Ring, stage depth, swizzle, descriptors and k order are those of the
 // gated and four-wave kernels, so all give the same bits.
-template <int NB0, int NB1, int ACT>
+//
+// BKM false takes B row-major ([K, N], n contiguous) at 352 columns: load q of
+// a wave then covers 64 consecutive 16-byte chunks of the stage's 32 x 352
+// block in row order (a 704-byte row pitch puts four consecutive rows on
+// disjoint banks), and a B fragment is two ds_read_b64_tr_b16 of four k rows.
+template <int NB0, int NB1, int ACT, bool BKM = true>
 __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   constexpr int BN = 32 * (NB0 + NB1);
+  static_assert(BKM || BN == 352, "row-major B at 352 columns only");
+  constexpr int BCH = BN / 8;                   // 16-byte chunks per row-major B row
   constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
   static_assert(DST * STAGE <= 160 * 1024, "the ring must fit in LDS");
   constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
@@ -827,9 +840,11 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const __bf16 *)p.a + (int64_t)m0 * p.lda), 0,
       (int)(((int64_t)(ra - 1) * p.lda + p.K) * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const __bf16 *)p.b + (int64_t)n0 * p.b_sn), 0,
-      (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs =
+      BKM ? __builtin_amdgcn_make_buffer_rsrc((void *)((const __bf16 *)p.b + (int64_t)n0 * p.b_sn), 0,
+                                              (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000)
+          : __builtin_amdgcn_make_buffer_rsrc((void *)((const __bf16 *)p.b + n0), 0,
+                                              (int)(((int64_t)(p.K - 1) * p.b_sk + rb) * 2), 0x00020000);
   // Lane i of a load fetches row i >> 2 of its 16-row group, logical chunk lc;
   // load q of a wave covers the 16-row group wave + 8 q of its operand.
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);
@@ -837,9 +852,14 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
 #pragma unroll
   for (int q = 0; q < LA; ++q)
     aoff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
+  // Row-major B: chunk 64 (wave + 8 q) + lane of a stage is row brow(q), columns
+  // bcol(q) .. + 7 (past the tile's last column: its last chunk again).
+  auto brow = [&](int q) { return (64 * (wave + 8 * q) + lane) / BCH; };
+  auto bcol = [&](int q) { return min(8 * ((64 * (wave + 8 * q) + lane) % BCH), rb - 8); };
 #pragma unroll
   for (int q = 0; q < LBH; ++q)
-    boff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc;
+    boff[q] = BKM ? (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc
+                  : (uint32_t)brow(q) * (uint32_t)p.b_sk * 2u + 2u * (uint32_t)bcol(q);
   const int nk = (p.K + DBK - 1) / DBK;
   typedef __attribute__((address_space(3))) void lds_void;
 
@@ -853,22 +873,39 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
     const bool whole = decltype(whole_c)::value || k0 + DBK <= p.K;
     const uint32_t kv = whole ? 0u : 2u * (uint32_t)min(k0 + 8 * lc, p.K - 8) - 16u * lc;
     const int ks = whole ? 2 * k0 : 0;
-    if (q < LA)
+    if (q < LA) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(sb + (wave + 8 * q) * 1024), 16, aoff[q] + kv,
                                                ks, 0, 0);
-    else if (q - LA < LBL || hi)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void *)(sb + A_BYTES + (wave + 8 * (q - LA)) * 1024), 16,
-                                               boff[q - LA] + kv, ks, 0, 0);
+    } else if (q - LA < LBL || hi) {
+      lds_void *dst = (lds_void *)(sb + A_BYTES + (wave + 8 * (q - LA)) * 1024);
+      if constexpr (BKM) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, dst, 16, boff[q - LA] + kv, ks, 0, 0);
+      } else if (whole) {   // the stage's first row in the scalar offset
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, dst, 16, boff[q - LA],
+                                                 (int)((uint32_t)k0 * (uint32_t)p.b_sk * 2u), 0, 0);
+      } else {              // K tail: a row past K fetches row K - 1, zeroed once landed
+        const uint32_t r = (uint32_t)min(k0 + brow(q - LA), p.K - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, dst, 16, r * (uint32_t)p.b_sk * 2u + 2u * (uint32_t)bcol(q - LA),
+                                                 0, 0, 0);
+      }
+    }
   };
   auto zero_tail = [&](int kt) {   // after stage kt (the K tail) has landed
+    char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
+    const u32x4 z = {0u, 0u, 0u, 0u};
     if (kt * DBK + 8 * lc >= p.K) {
-      char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
-      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int q = 0; q < LA; ++q) *(u32x4 *)(sb + (wave + 8 * q) * 1024) = z;
+      if constexpr (BKM) {
+#pragma unroll
+        for (int q = 0; q < LBH; ++q)
+          if (q < LBL || hi) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+      }
+    }
+    if constexpr (!BKM) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
-        if (q < LBL || hi) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+        if ((q < LBL || hi) && kt * DBK + brow(q) >= p.K) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
     }
   };
   // this wave's loads of the oldest stage in flight have landed (the two
@@ -890,6 +927,9 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
     constexpr int NM = 4 * NBW, PD = 4;
     static_assert(PD % 2 == 0 && PD <= 2 * NBW, "reads run ahead within one k-step");
     const int rowb = A_BYTES + (col0 + l32) * 64;
+    // row-major B: this lane's transposing-read address in a stage (k row
+    // 8 h2 + (lane & 15) / 4, column col0 + 16 ((lane >> 4) & 1) + 4 (lane & 3))
+    const int trb = A_BYTES + ((8 * h2 + ((lane & 15) >> 2)) * BN + col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     bf16x8 fa[2][2], fb[2][NBW];
     f32x16 acc[2][NBW];
 #pragma unroll
@@ -903,7 +943,15 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
         fa[ks][0] = *(const bf16x8 *)(b + rowa);
         fa[ks][1] = *(const bf16x8 *)(b + rowa + 2048);
       }
-      if (r % 2 == 0) fb[ks][r / 2] = *(const bf16x8 *)(b + rowb + (r / 2) * 2048);
+      if (r % 2 == 0) {
+        if constexpr (BKM) {
+          fb[ks][r / 2] = *(const bf16x8 *)(b + rowb + (r / 2) * 2048);
+        } else {   // k rows 16 ks + 8 h2 + 0..3, then + 4..7, of column block r / 2
+          const __bf16 *src = (const __bf16 *)(sb + trb + ks * 16 * 2 * BN + (r / 2) * 64);
+          const i16x4 lo = ds_read_tr(src), hi4 = ds_read_tr(src + 4 * BN);
+          fb[ks][r / 2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
     };
     auto run = [&](auto whole_c) {
       constexpr bool WHOLE = decltype(whole_c)::value;
@@ -953,14 +1001,15 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   else body(std::integral_constant<int, NB1>{}, 32 * NB0);
 }
 
-#define CHAIN_W8R_KERNEL(NAME, NB0, NB1, ACT)                                                 \
+#define CHAIN_W8R_KERNEL(NAME, NB0, NB1, ACT, BKM)                                            \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
-  void NAME(const GemmParams p) { gemm_bf16_w8r<NB0, NB1, ACT>(p); }
+  void NAME(const GemmParams p) { gemm_bf16_w8r<NB0, NB1, ACT, BKM>(p); }
 #define CHAIN_W8R_KERNELS(SUFFIX, ACT)                                 \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_4_##SUFFIX, 2, 2, ACT)         \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_6_##SUFFIX, 3, 3, ACT)         \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_8_##SUFFIX, 4, 4, ACT)         \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_##SUFFIX, 6, 5, ACT)
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_4_##SUFFIX, 2, 2, ACT, true)   \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_6_##SUFFIX, 3, 3, ACT, true)   \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_8_##SUFFIX, 4, 4, ACT, true)   \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_##SUFFIX, 6, 5, ACT, true)  \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_11_##SUFFIX, 6, 5, ACT, false)
 CHAIN_W8R_KERNELS(erf, CHAIN_ACT_GELU_ERF)
 CHAIN_W8R_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
 CHAIN_W8R_KERNELS(id, CHAIN_ACT_IDENTITY)
@@ -1109,6 +1158,23 @@ void launch_w8(const GemmParams &p, int nbw, hipStream_t stream) {
   hipLaunchKernelGGL(ks[nbw == 11 ? 3 : nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
 }
 
+// Row-major B (n contiguous) at 352 columns on the eight-wave kernel: B's
+// rows and the base 16-byte aligned, N a multiple of 8, and the whole of B's
+// column band within 32-bit byte offsets.
+bool w8rt_fits(const GemmParams &p) {
+  const int64_t span_a = ((int64_t)(min(p.M, BM) - 1) * p.lda + p.K) * 2;
+  const int64_t span_b = ((int64_t)(p.K - 1) * p.b_sk + min(p.N, 352)) * 2;
+  return p.b_sn == 1 && (uintptr_t)p.b % 16 == 0 && p.b_sk % 8 == 0 && p.N % 8 == 0 &&
+         span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
+}
+void launch_w8rt(const GemmParams &p, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 351) / 352);
+  typedef void (*Kern)(const GemmParams);
+  static const Kern ks[4] = {gemm_bf16_w8rt_kernel_11_erf, gemm_bf16_w8rt_kernel_11_tanh,
+                             gemm_bf16_w8rt_kernel_11_id, gemm_bf16_w8rt_kernel_11_silu};
+  hipLaunchKernelGGL(ks[p.act], dim3(tiles), dim3(512), 0, stream, p);
+}
+
 int compute_units() {
   static thread_local int dev_cached = -1, cus = 256;
   int dev = 0;
@@ -1149,12 +1215,14 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
     if (dtype != CHAIN_BF16 || p.b_sk != 1) return hipErrorInvalidValue;
     launch_dtl_gated(p, compute_units(), stream);
   } else if (dtype == CHAIN_BF16) {
-    const bool k_contig = p.b_sk == 1;
-    const int choice = gemm_bf16_block_cols(p.M, p.N, compute_units(), k_contig);
+    const bool k_contig = p.b_sk == 1, rt = !k_contig && w8rt_fits(p);
+    const int choice = gemm_bf16_block_cols(p.M, p.N, compute_units(), k_contig || rt);
     const int nbw = choice == 11 ? 4 : choice;
     if (k_contig) {
       if (rows_fit32(p, choice == 11 ? 352 : 64 * nbw)) launch_w8(p, choice, stream);
       else launch_dtl(p, nbw, stream);
+    } else if (rt && choice == 11) {
+      launch_w8rt(p, stream);
     } else {
       launch_bf16_width(p, nbw, stream);
     }

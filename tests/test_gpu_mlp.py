@@ -65,9 +65,9 @@ def _rounds_x_width(M, N, width, cus=256):
 def test_mlp_wide_tiles_ragged():
     """An X.W1 whose inner width takes the 352-wide uneven tiles on a 256-CU chip
     (one round, where 128-, 192- and 256-wide tiles need two or three), with a
-    ragged last row tile, a ragged last column tile and a K tail; k-major weights
-    take those tiles, row-major ones the register-staged kernel, and both must
-    give the same bits."""
+    ragged last row tile, a ragged last column tile and a K tail; k-major and
+    row-major weights both take those tiles (B staged per column or per k row)
+    and must give the same bits."""
     M, K, N, K2 = 8092, 4104, 2792, 512
     assert _rounds_x_width(M, N, 352) < min(_rounds_x_width(M, N, w) for w in (128, 192, 256))
     dev = device()
@@ -83,6 +83,34 @@ def test_mlp_wide_tiles_ragged():
     rows = sample_rows(M, 120, 53, extra=(0, 255, 256, 7935, 7936, M - 1))
     ref = oracle.mlp(f64(x[rows]), f64(w1), f64(w2), "gelu_erf")
     err = max_abs(f64(o_k.cpu()[rows]), ref)
+    print(f"max-abs {err:.3e} over {len(rows)} rows")
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("K,pad", [(24, 0), (4104, 40), (64, 8)])
+def test_mlp_row_major_wide_tiles_edges(K, pad):
+    """Row-major weights on the 352-wide tiles: a last column tile of 8 columns
+    (N = 7 x 352 + 8), K within one partial stage (24), a K tail after whole
+    stages (4104) and whole stages only (64), W1 rows padded past N (a view of
+    a wider array); the bits must equal those of k-major weights."""
+    M, N, K2 = 8092, 7 * 352 + 8, 264
+    assert _rounds_x_width(M, N, 352) < min(_rounds_x_width(M, N, w) for w in (128, 192, 256))
+    dev = device()
+    if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
+        pytest.skip("the tile choice asserted here assumes 256 compute units")
+    x, w1, w2 = gen_mlp(M, K, N, K2, dtype="bf16", amp_x=1.0, amp_w=0.02, seed=70 + K % 89)
+    announce(f"mlp row-major wide tiles M{M} K{K} N{N} K2{K2} pad {pad}")
+    xd, w2d = x.to(dev), w2.to(dev)
+    w1p = torch.zeros(K, N + pad, dtype=w1.dtype, device=dev)
+    w1p[:, :N] = w1.to(dev)
+    w1d = w1p[:, :N]
+    o_row = chain.mlp_fwd(xd, w1d, w2d, act="gelu_tanh")
+    o_k = chain.mlp_fwd(xd, _kmajor(w1d), _kmajor(w2d), act="gelu_tanh")
+    torch.cuda.synchronize()
+    assert torch.equal(o_row, o_k)
+    rows = sample_rows(M, 64, 70, extra=(0, 255, 256, 7935, 7936, M - 1))
+    ref = oracle.mlp(f64(x[rows]), f64(w1), f64(w2), "gelu_tanh")
+    err = max_abs(f64(o_row.cpu()[rows]), ref)
     print(f"max-abs {err:.3e} over {len(rows)} rows")
     assert err <= TOL_BF16
 
