@@ -808,15 +808,20 @@ CHAIN_W8_KERNELS(silu, CHAIN_ACT_SILU)
 // next.  Ring, stage depth, swizzle, descriptors and k order are those of the
 // gated and four-wave kernels, so all give the same bits.
 //
-// BKM false takes B row-major ([K, N], n contiguous) at 352 columns: load q of
-// a wave then covers 64 consecutive 16-byte chunks of the stage's 32 x 352
-// block in row order (a 704-byte row pitch puts four consecutive rows on
-// disjoint banks), and a B fragment is two ds_read_b64_tr_b16 of four k rows.
+// BKM false takes B row-major ([K, N], n contiguous): load q of a wave then
+// covers 64 consecutive 16-byte chunks of the stage's 32 x BN block in row
+// order, and a B fragment is two ds_read_b64_tr_b16 of four k rows.  A
+// transposing read takes 64 bytes (a 64-byte group) of each of four
+// consecutive rows; the groups of row r are XOR-swizzled by row_swz(r) so that
+// the four land on disjoint banks (at 352 columns the 704-byte pitch already
+// does that).
 template <int NB0, int NB1, int ACT, bool BKM = true>
 __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   constexpr int BN = 32 * (NB0 + NB1);
-  static_assert(BKM || BN == 352, "row-major B at 352 columns only");
-  constexpr int BCH = BN / 8;                   // 16-byte chunks per row-major B row
+  constexpr int BCH = BN / 8, BG = BN / 32;     // 16-byte chunks, 64-byte groups per row-major B row
+  // Pitch 64 BG bytes: rows r..r+3 start 16 BG banks apart.  BG = 0 mod 4: all
+  // on one bank group, swizzle by r & 3; BG = 2 mod 4: two apart, by (r >> 1) & 1.
+  auto row_swz = [](int r) { return BG % 4 == 0 ? (r & 3) : BG % 4 == 2 ? ((r >> 1) & 1) : 0; };
   constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
   static_assert(DST * STAGE <= 160 * 1024, "the ring must fit in LDS");
   constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
@@ -855,7 +860,10 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   // Row-major B: chunk 64 (wave + 8 q) + lane of a stage is row brow(q), columns
   // bcol(q) .. + 7 (past the tile's last column: its last chunk again).
   auto brow = [&](int q) { return (64 * (wave + 8 * q) + lane) / BCH; };
-  auto bcol = [&](int q) { return min(8 * ((64 * (wave + 8 * q) + lane) % BCH), rb - 8); };
+  auto bcol = [&](int q) {
+    const int c = (64 * (wave + 8 * q) + lane) % BCH;
+    return min(8 * (4 * ((c >> 2) ^ row_swz(brow(q))) + (c & 3)), rb - 8);
+  };
 #pragma unroll
   for (int q = 0; q < LBH; ++q)
     boff[q] = BKM ? (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc
@@ -927,9 +935,17 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
     constexpr int NM = 4 * NBW, PD = 4;
     static_assert(PD % 2 == 0 && PD <= 2 * NBW, "reads run ahead within one k-step");
     const int rowb = A_BYTES + (col0 + l32) * 64;
-    // row-major B: this lane's transposing-read address in a stage (k row
-    // 8 h2 + (lane & 15) / 4, column col0 + 16 ((lane >> 4) & 1) + 4 (lane & 3))
-    const int trb = A_BYTES + ((8 * h2 + ((lane & 15) >> 2)) * BN + col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    // row-major B: this lane's transposing-read address within a stage for
+    // column block j: k row 8 h2 + (lane & 15) / 4, column col0 + 32 j +
+    // 16 ((lane >> 4) & 1) + 4 (lane & 3), its 64-byte group swizzled
+    int trb[NBW];
+    {
+      const int tr = (lane & 15) >> 2;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        trb[j] = A_BYTES + (8 * h2 + tr) * 2 * BN + (((col0 >> 5) + j) ^ row_swz(tr)) * 64 +
+                 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    }
     bf16x8 fa[2][2], fb[2][NBW];
     f32x16 acc[2][NBW];
 #pragma unroll
@@ -947,7 +963,7 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
         if constexpr (BKM) {
           fb[ks][r / 2] = *(const bf16x8 *)(b + rowb + (r / 2) * 2048);
         } else {   // k rows 16 ks + 8 h2 + 0..3, then + 4..7, of column block r / 2
-          const __bf16 *src = (const __bf16 *)(sb + trb + ks * 16 * 2 * BN + (r / 2) * 64);
+          const __bf16 *src = (const __bf16 *)(sb + trb[r / 2] + ks * 16 * 2 * BN);
           const i16x4 lo = ds_read_tr(src), hi4 = ds_read_tr(src + 4 * BN);
           fb[ks][r / 2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         }
@@ -1009,6 +1025,9 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_6_##SUFFIX, 3, 3, ACT, true)   \
   CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_8_##SUFFIX, 4, 4, ACT, true)   \
   CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_##SUFFIX, 6, 5, ACT, true)  \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_4_##SUFFIX, 2, 2, ACT, false) \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_6_##SUFFIX, 3, 3, ACT, false) \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_8_##SUFFIX, 4, 4, ACT, false) \
   CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_11_##SUFFIX, 6, 5, ACT, false)
 CHAIN_W8R_KERNELS(erf, CHAIN_ACT_GELU_ERF)
 CHAIN_W8R_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
@@ -1158,21 +1177,29 @@ void launch_w8(const GemmParams &p, int nbw, hipStream_t stream) {
   hipLaunchKernelGGL(ks[nbw == 11 ? 3 : nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
 }
 
-// Row-major B (n contiguous) at 352 columns on the eight-wave kernel: B's
-// rows and the base 16-byte aligned, N a multiple of 8, and the whole of B's
-// column band within 32-bit byte offsets.
+// Row-major B (n contiguous) on the eight-wave kernel: B's rows and base
+// 16-byte aligned, N a multiple of 8, and B's column band of the widest tile
+// within 32-bit byte offsets.
 bool w8rt_fits(const GemmParams &p) {
   const int64_t span_a = ((int64_t)(min(p.M, BM) - 1) * p.lda + p.K) * 2;
   const int64_t span_b = ((int64_t)(p.K - 1) * p.b_sk + min(p.N, 352)) * 2;
   return p.b_sn == 1 && (uintptr_t)p.b % 16 == 0 && p.b_sk % 8 == 0 && p.N % 8 == 0 &&
          span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
 }
-void launch_w8rt(const GemmParams &p, hipStream_t stream) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 351) / 352);
+void launch_w8rt(const GemmParams &p, int nbw, hipStream_t stream) {
+  const int width = nbw == 11 ? 352 : 64 * nbw;
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + width - 1) / width);
   typedef void (*Kern)(const GemmParams);
-  static const Kern ks[4] = {gemm_bf16_w8rt_kernel_11_erf, gemm_bf16_w8rt_kernel_11_tanh,
-                             gemm_bf16_w8rt_kernel_11_id, gemm_bf16_w8rt_kernel_11_silu};
-  hipLaunchKernelGGL(ks[p.act], dim3(tiles), dim3(512), 0, stream, p);
+  static const Kern ks[4][4] = {
+      {gemm_bf16_w8rt_kernel_4_erf, gemm_bf16_w8rt_kernel_4_tanh, gemm_bf16_w8rt_kernel_4_id,
+       gemm_bf16_w8rt_kernel_4_silu},
+      {gemm_bf16_w8rt_kernel_6_erf, gemm_bf16_w8rt_kernel_6_tanh, gemm_bf16_w8rt_kernel_6_id,
+       gemm_bf16_w8rt_kernel_6_silu},
+      {gemm_bf16_w8rt_kernel_8_erf, gemm_bf16_w8rt_kernel_8_tanh, gemm_bf16_w8rt_kernel_8_id,
+       gemm_bf16_w8rt_kernel_8_silu},
+      {gemm_bf16_w8rt_kernel_11_erf, gemm_bf16_w8rt_kernel_11_tanh, gemm_bf16_w8rt_kernel_11_id,
+       gemm_bf16_w8rt_kernel_11_silu}};
+  hipLaunchKernelGGL(ks[nbw == 11 ? 3 : nbw - 2][p.act], dim3(tiles), dim3(512), 0, stream, p);
 }
 
 int compute_units() {
@@ -1221,8 +1248,8 @@ hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
     if (k_contig) {
       if (rows_fit32(p, choice == 11 ? 352 : 64 * nbw)) launch_w8(p, choice, stream);
       else launch_dtl(p, nbw, stream);
-    } else if (rt && choice == 11) {
-      launch_w8rt(p, stream);
+    } else if (rt) {
+      launch_w8rt(p, choice, stream);
     } else {
       launch_bf16_width(p, nbw, stream);
     }

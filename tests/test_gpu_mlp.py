@@ -141,12 +141,13 @@ def _kmajor(w):
     return w.t().contiguous().t()
 
 
-# On a 256-CU device these shapes select each bf16 tile width: N = 1376 over
-# 63 row tiles takes 192-wide tiles, N = 4096 takes 256-wide ones, small
-# problems 128-wide.  M, N or K is ragged in each.
+# On a 256-CU device these shapes select each bf16 tile width (for X.W1, then
+# H.W2): 352 and 352, 256 and 128, 192 and 128, 128 for the small problems.
+# M, N or K is ragged in each.
 @pytest.mark.parametrize("M,K,N,K2", [
     (16000, 4096, 1376, 4096),
     (4000, 1376, 4096, 264),
+    (17900, 72, 1152, 264),     # 192-wide tiles for X.W1, a K tail after two stages
     (300, 200, 136, 264),
     (96, 8, 24, 40),            # K and N below one 32-deep stage: only K-tail stages
     (16000, 4008, 1376, 264),   # 192-wide tiles (uneven loads of B per wave) with a K tail
