@@ -529,11 +529,16 @@ chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg, 
   if (K % 8 || N % 8 || K2 % 8) return fail(CHAIN_ERR_UNSUPPORTED, "K, N and K2 must be multiples of 8");
   if (M > INT32_MAX || K > INT32_MAX || N > INT32_MAX || K2 > INT32_MAX)
     return fail(CHAIN_ERR_UNSUPPORTED, "sizes beyond 2^31");
-  // Gate and up weights: k contiguous, one column stride for both.
+  // Gate and up weights: one layout and one stride for both, k contiguous
+  // (column-major) or n contiguous (row-major).
   auto kmajor = [](const chain_tensor &w) { return w.shape[0] <= 1 || w.stride[0] == 1; };
+  auto nmajor = [](const chain_tensor &w) { return w.shape[1] <= 1 || w.stride[1] == 1; };
   const int64_t gsn = Wg->shape[1] <= 1 ? K : Wg->stride[1], usn = Wu->shape[1] <= 1 ? K : Wu->stride[1];
-  if (K > 0 && N > 0 && (!kmajor(*Wg) || !kmajor(*Wu) || gsn != usn))
-    return fail(CHAIN_ERR_UNSUPPORTED, "gate and up weights must be column-major with equal strides");
+  const int64_t gsk = Wg->shape[0] <= 1 ? N : Wg->stride[0], usk = Wu->shape[0] <= 1 ? N : Wu->stride[0];
+  const bool gu_k = kmajor(*Wg) && kmajor(*Wu) && gsn == usn;
+  const bool gu_n = !gu_k && nmajor(*Wg) && nmajor(*Wu) && gsk == usk;
+  if (K > 0 && N > 0 && !gu_k && !gu_n)
+    return fail(CHAIN_ERR_UNSUPPORTED, "gate and up weights must share one layout (row- or column-major) and strides");
   if (overlap(*O, *X) || overlap(*O, *Wg) || overlap(*O, *Wu) || overlap(*O, *Wd))
     return fail(CHAIN_ERR_ALIAS, "O overlaps an input");
   const size_t need = chain_mlp_workspace_bytes(M, N, CHAIN_BF16);
@@ -555,7 +560,8 @@ chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg, 
   chain::GemmParams g1{}, g2{};
   g1.a = X->data, g1.b = Wg->data, g1.b2 = Wu->data, g1.gated = 1, g1.c = workspace;
   g1.lda = X->stride[0], g1.ldc = N;
-  g1.b_sk = 1, g1.b_sn = gsn;
+  if (gu_n) g1.b_sk = gsk, g1.b_sn = 1;
+  else g1.b_sk = 1, g1.b_sn = gsn;
   g1.M = (int32_t)M, g1.N = (int32_t)N, g1.K = (int32_t)K;
   g1.act = act;
   g1.c_f32 = 0;
@@ -570,8 +576,10 @@ chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg, 
   g2.c_f32 = O->dtype == CHAIN_F32;
   g2.c_vec = (uintptr_t)O->data % (4 * oes) == 0 && (M <= 1 || (O->stride[0] * oes) % (4 * oes) == 0);
   const int64_t kMaxStride = int64_t(1) << 25;   // per-thread offsets within a tile stay 32-bit
-  for (const int64_t st : {g1.lda, g1.b_sn, g2.b_sk, g2.b_sn, g2.ldc})
+  for (const int64_t st : {g1.lda, g1.b_sk, g1.b_sn, g2.b_sk, g2.b_sn, g2.ldc})
     if (st > kMaxStride) return fail(CHAIN_ERR_UNSUPPORTED, "row strides beyond 2^25 elements");
+  if (gu_n && N > 0 && K > 0 && !chain::gemm_gated_rowmajor_ok(g1))
+    return fail(CHAIN_ERR_UNSUPPORTED, "row-major gate and up weights: rows beyond 32-bit offsets");
   hipError_t e = hipSuccess;
   if (N > 0) e = chain::launch_gemm(g1, CHAIN_BF16, (hipStream_t)stream);
   if (e == hipSuccess) e = chain::launch_gemm(g2, CHAIN_BF16, (hipStream_t)stream);

@@ -592,7 +592,13 @@ CHAIN_DTL_KERNELS(silu, CHAIN_ACT_SILU)
 // a tile's rows span less than 2^31 bytes), with the stage's k offset in the
 // scalar offset operand.  A second wave on each SIMD issues MFMAs while the
 // other waits on its fragment reads or the barrier.
-template <int NBW, bool GATED, int ACT>
+//
+// BKM false (gated only) takes the gate and up weights row-major ([K, N], n
+// contiguous, one row stride): a stage's B block is then two row-major 32 x OBN
+// sub-blocks, gate then up, each filled by whole 1 KB loads (so every load
+// reads through one descriptor) with 64-byte groups XOR-swizzled by row as in
+// gemm_bf16_w8r, and read with ds_read_b64_tr_b16.
+template <int NBW, bool GATED, int ACT, bool BKM = true>
 __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   constexpr int BN = 64 * NBW, WTN = 32 * NBW;
   constexpr int OBN = GATED ? BN / 2 : BN;   // output columns per tile
@@ -601,6 +607,10 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
   constexpr int LA = BM / 16 / 8;               // 1 KB loads of A per wave and stage
   constexpr int LBH = (NLB + 7) / 8, LBL = NLB / 8;   // of B: waves below NLB % 8 take LBH
+  static_assert(BKM || GATED, "row-major B: gated tiles only (a load never spans the two sub-blocks)");
+  constexpr int BCH = OBN / 8, BG = OBN / 32;   // row-major sub-block: 16-byte chunks, 64-byte groups per row
+  constexpr int SUB = DBK * OBN * 2;            // bytes of a row-major sub-block
+  auto row_swz = [](int r) { return BG % 4 == 0 ? (r & 3) : BG % 4 == 2 ? ((r >> 1) & 1) : 0; };
   __shared__ __attribute__((aligned(1024))) char lds[DST * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -621,12 +631,12 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const __bf16 *)p.a + (int64_t)m0 * p.lda), 0,
       (int)(((int64_t)(ra - 1) * p.lda + p.K) * 2), 0x00020000);
+  const int64_t bspan = BKM ? (int64_t)(rb - 1) * p.b_sn + p.K : (int64_t)(p.K - 1) * p.b_sk + rb;
+  const int64_t bbase = BKM ? (int64_t)n0 * p.b_sn : n0;
   const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const __bf16 *)p.b + (int64_t)n0 * p.b_sn), 0,
-      (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000);
+      (void *)((const __bf16 *)p.b + bbase), 0, (int)(bspan * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t brs2 = GATED ? __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const __bf16 *)p.b2 + (int64_t)n0 * p.b_sn), 0,
-      (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000) : brs;
+      (void *)((const __bf16 *)p.b2 + bbase), 0, (int)(bspan * 2), 0x00020000) : brs;
   // Staged B row r holds output column n0 + bcol(r) of B, or (gated) of B2 when
   // bup(r): each wave's 32-row blocks alternate gate, up for the same 32 columns.
   auto bcol = [](int r) {
@@ -640,9 +650,21 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 #pragma unroll
   for (int q = 0; q < LA; ++q)
     aoff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
+  // Row-major: load L = wave + 8 q fills sub-block L / (NLB / 2) (gate, up);
+  // its lane takes chunk g of the sub-block, row brow(q), columns bcolr(q) ..+7
+  // (past the tile's last column: its last chunk again).
+  auto bsub = [&](int q) { return (wave + 8 * q) / (NLB / 2); };
+  auto brow = [&](int q) { return (64 * ((wave + 8 * q) % (NLB / 2)) + lane) / BCH; };
+  auto bcolr = [&](int q) {
+    const int c = (64 * ((wave + 8 * q) % (NLB / 2)) + lane) % BCH;
+    return min(8 * (4 * ((c >> 2) ^ row_swz(brow(q))) + (c & 3)), rb - 8);
+  };
 #pragma unroll
   for (int q = 0; q < LBH; ++q)
-    boff[q] = (uint32_t)min(bcol(16 * (wave + 8 * q) + (lane >> 2)), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc;
+    boff[q] = BKM ? (uint32_t)min(bcol(16 * (wave + 8 * q) + (lane >> 2)), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc
+                  : (uint32_t)brow(q) * (uint32_t)p.b_sk * 2u + 2u * (uint32_t)bcolr(q);
+  // the descriptor of load q: k-major, by its staged rows; row-major, by its sub-block
+  auto bdesc = [&](int q) { return (BKM ? bup(16 * (wave + 8 * q)) : bsub(q) == 1) ? brs2 : brs; };
   const int nk = (p.K + DBK - 1) / DBK;
   typedef __attribute__((address_space(3))) void lds_void;
 
@@ -659,9 +681,23 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
         if (q < LBL || hi)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(bup(16 * (wave + 8 * q)) ? brs2 : brs,
-                                                   (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
-                                                   boff[q], 2 * k0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              bdesc(q), (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16, boff[q],
+              BKM ? 2 * k0 : (int)((uint32_t)k0 * (uint32_t)p.b_sk * 2u), 0, 0);
+    } else if constexpr (!BKM) {
+      // K tail: A chunks past K fetch k = K - 8 of their row, B rows past K row K - 1
+      const uint32_t kb = 2u * (uint32_t)min(k0 + 8 * lc, p.K - 8) - 16u * lc;
+#pragma unroll
+      for (int q = 0; q < LA; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(sb + (wave + 8 * q) * 1024), 16, aoff[q] + kb,
+                                                 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < LBH; ++q)
+        if (q < LBL || hi) {
+          const uint32_t r = (uint32_t)min(k0 + brow(q), p.K - 1);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bdesc(q), (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
+                                                   r * (uint32_t)p.b_sk * 2u + 2u * (uint32_t)bcolr(q), 0, 0, 0);
+        }
     } else {
       // K tail: a chunk past K fetches k = K - 8 of its row instead
       const uint32_t kb = 2u * (uint32_t)min(k0 + 8 * lc, p.K - 8) - 16u * lc;
@@ -679,14 +715,21 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   };
   // After stage kt (the K tail) has landed: zero the chunks past K.
   auto zero_tail = [&](int kt) {
+    char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
+    const u32x4 z = {0u, 0u, 0u, 0u};
     if (kt * DBK + 8 * lc >= p.K) {
-      char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
-      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int q = 0; q < LA; ++q) *(u32x4 *)(sb + (wave + 8 * q) * 1024) = z;
+      if constexpr (BKM) {
+#pragma unroll
+        for (int q = 0; q < LBH; ++q)
+          if (q < LBL || hi) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+      }
+    }
+    if constexpr (!BKM) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
-        if (q < LBL || hi) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+        if ((q < LBL || hi) && kt * DBK + brow(q) >= p.K) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
     }
   };
   // This wave's loads of stage s have landed (stages s+1 and s+2 may still be
@@ -703,12 +746,30 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   const int sx = (l32 >> 2) & 3;
   const int pc0 = (h2 ^ sx) * 16, pc1 = ((2 + h2) ^ sx) * 16;
   const int rowa = (wm * 64 + l32) * 64, rowb = A_BYTES + (wn * WTN + l32) * 64;
+  // row-major: the transposing-read address of block j (gate for even j, up
+  // for odd, output column block wn NBW / 2 + j / 2): k row 8 h2 + (lane & 15) / 4
+  int trb[NBW];
+  if constexpr (!BKM) {
+    const int tr = (lane & 15) >> 2;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+      trb[j] = A_BYTES + (j & 1) * SUB + (8 * h2 + tr) * 2 * OBN + ((wn * (NBW / 2) + (j >> 1)) ^ row_swz(tr)) * 64 +
+               2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  }
   auto frags = [&](int kt, int ks, Frags &f) {
     const char *sb = lds + (kt & (DST - 1)) * STAGE + (ks ? pc1 : pc0);
 #pragma unroll
     for (int i = 0; i < 2; ++i) f.a[i] = *(const bf16x8 *)(sb + rowa + i * 2048);
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) f.b[j] = *(const bf16x8 *)(sb + rowb + j * 2048);
+    for (int j = 0; j < NBW; ++j) {
+      if constexpr (BKM) {
+        f.b[j] = *(const bf16x8 *)(sb + rowb + j * 2048);
+      } else {   // k rows 16 ks + 8 h2 + 0..3, then + 4..7
+        const __bf16 *src = (const __bf16 *)(lds + (kt & (DST - 1)) * STAGE + trb[j] + ks * 16 * 2 * OBN);
+        const i16x4 lo = ds_read_tr(src), hi4 = ds_read_tr(src + 4 * OBN);
+        f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
   };
 
   f32x16 acc[2][NBW];
@@ -780,12 +841,14 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   gemm_store_tile<2, NBW, GATED, ACT>(p, acc, m0 + wm * 64, n0 + wn * (GATED ? WTN / 2 : WTN), l32, h2);
 }
 
-#define CHAIN_W8_KERNEL(NAME, NBW, GATED, ACT)                                                \
+#define CHAIN_W8_KERNEL(NAME, NBW, GATED, ACT, BKM)                                           \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
-  void NAME(const GemmParams p) { gemm_bf16_w8<NBW, GATED, ACT>(p); }
-#define CHAIN_W8_KERNELS(SUFFIX, ACT)                                    \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_2_##SUFFIX, 2, true, ACT)    \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_4_##SUFFIX, 4, true, ACT)
+  void NAME(const GemmParams p) { gemm_bf16_w8<NBW, GATED, ACT, BKM>(p); }
+#define CHAIN_W8_KERNELS(SUFFIX, ACT)                                           \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_2_##SUFFIX, 2, true, ACT, true)     \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_4_##SUFFIX, 4, true, ACT, true)     \
+  CHAIN_W8_KERNEL(gemm_bf16_w8t_gated_kernel_2_##SUFFIX, 2, true, ACT, false)   \
+  CHAIN_W8_KERNEL(gemm_bf16_w8t_gated_kernel_4_##SUFFIX, 4, true, ACT, false)
 CHAIN_W8_KERNELS(erf, CHAIN_ACT_GELU_ERF)
 CHAIN_W8_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
 CHAIN_W8_KERNELS(id, CHAIN_ACT_IDENTITY)
@@ -1137,6 +1200,14 @@ void launch_dtl_gated(const GemmParams &p, int cus, hipStream_t stream) {
   const int nbw = cost(2) < cost(4) ? 2 : 4;
   const int tiles = tm * ((p.N + 32 * nbw - 1) / (32 * nbw));
   typedef void (*Kern)(const GemmParams);
+  if (p.b_sk != 1) {   // row-major gate and up weights (gemm_gated_rowmajor_ok holds)
+    static const Kern t2[4] = {gemm_bf16_w8t_gated_kernel_2_erf, gemm_bf16_w8t_gated_kernel_2_tanh,
+                               gemm_bf16_w8t_gated_kernel_2_id, gemm_bf16_w8t_gated_kernel_2_silu};
+    static const Kern t4[4] = {gemm_bf16_w8t_gated_kernel_4_erf, gemm_bf16_w8t_gated_kernel_4_tanh,
+                               gemm_bf16_w8t_gated_kernel_4_id, gemm_bf16_w8t_gated_kernel_4_silu};
+    hipLaunchKernelGGL((nbw == 4 ? t4 : t2)[p.act], dim3(tiles), dim3(512), 0, stream, p);
+    return;
+  }
   if (w8_fits(p, nbw, true)) {
     static const Kern w2[4] = {gemm_bf16_w8_gated_kernel_2_erf, gemm_bf16_w8_gated_kernel_2_tanh,
                                gemm_bf16_w8_gated_kernel_2_id, gemm_bf16_w8_gated_kernel_2_silu};
@@ -1236,10 +1307,17 @@ int gemm_bf16_block_cols(int M, int N, int cus, bool wide) {
   return best;
 }
 
+bool gemm_gated_rowmajor_ok(const GemmParams &p) {
+  const int64_t span_a = ((int64_t)(min(p.M, BM) - 1) * p.lda + p.K) * 2;
+  const int64_t span_b = ((int64_t)(p.K - 1) * p.b_sk + min(p.N, 128)) * 2;
+  return p.b_sn == 1 && (uintptr_t)p.b % 16 == 0 && (uintptr_t)p.b2 % 16 == 0 && p.b_sk % 8 == 0 &&
+         p.N % 8 == 0 && span_a < ((int64_t)1 << 31) && span_b < ((int64_t)1 << 31);
+}
+
 hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   if (p.gated) {
-    if (dtype != CHAIN_BF16 || p.b_sk != 1) return hipErrorInvalidValue;
+    if (dtype != CHAIN_BF16 || (p.b_sk != 1 && !gemm_gated_rowmajor_ok(p))) return hipErrorInvalidValue;
     launch_dtl_gated(p, compute_units(), stream);
   } else if (dtype == CHAIN_BF16) {
     const bool k_contig = p.b_sk == 1, rt = !k_contig && w8rt_fits(p);

@@ -165,8 +165,8 @@ struct GemmParams {
   int32_t act;        // chain_act
   int32_t c_f32;      // 1: C is f32, 0: C is bf16
   int32_t c_vec;      // 1: C rows allow 4-element vector stores (aligned base and ldc)
-  const void *b2;     // gated: the up weights, strides of b (k contiguous); C = act(A.B) * (A.B2)
-  int32_t gated;      // 1: the gated product above (bf16, b_sk == 1 only)
+  const void *b2;     // gated: the up weights, strides of b; C = act(A.B) * (A.B2)
+  int32_t gated;      // 1: the gated product above (bf16; b_sk == 1, or b_sn == 1 and gemm_gated_rowmajor_ok)
 };
 
 struct AttnBwdParams {
@@ -215,6 +215,10 @@ hipError_t launch_attn_mfma_bf16(const AttnParams &p, int D, hipStream_t stream)
 hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 hipError_t launch_gemm(const GemmParams &p, int dtype, hipStream_t stream);
+// Gated, with row-major gate and up weights (b_sn == 1): whether the kernel
+// takes them (16-byte aligned bases, row stride and N multiples of 8, a tile's
+// rows within 32-bit byte offsets).
+bool gemm_gated_rowmajor_ok(const GemmParams &p);
 hipError_t launch_attn_bwd(const AttnBwdParams &p, int D, hipStream_t stream);
 hipError_t launch_linear_attn(const LinAttnParams &p, int D, hipStream_t stream);
 size_t linear_attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D);

@@ -243,9 +243,10 @@ chain_status chain_mlp_fwd_noalloc(const chain_tensor *X, const chain_tensor *W1
  * realmente significa plegar"); the activation acts on the gate product only.
  *
  *   X      [M, K]    bf16 (input, row-major)
- *   Wg, Wu [K, N]    bf16 (input), column-major (stride (1, ld)): the transpose of
- *                    row-major [N, K] weights, as linear layers store them; both
- *                    with the same strides
+ *   Wg, Wu [K, N]    bf16 (input), both column-major (stride (1, ld)): the
+ *                    transpose of row-major [N, K] weights, as linear layers store
+ *                    them; or both row-major (stride (ld, 1)); the two with the
+ *                    same strides
  *   Wd     [N, K2]   bf16 (input), row- or column-major as W2 of chain_mlp_fwd
  *   O      [M, K2]   bf16 or f32 (output, row-major)
  *   act    a chain_act (CHAIN_ACT_SILU is the usual gate)
@@ -253,8 +254,10 @@ chain_status chain_mlp_fwd_noalloc(const chain_tensor *X, const chain_tensor *W1
  *              bytes, 256-byte aligned, holding H = act(X.Wg) * (X.Wu) in bf16
  *              (rounded to nearest even after the f32 product).
  * One kernel computes both products of a tile and the gate in its epilogue;
- * accumulation is f32.  K, N, K2 multiples of 8; f32 inputs or row-major gate/up
- * weights give CHAIN_ERR_UNSUPPORTED.  Other conventions as chain_mlp_fwd.
+ * accumulation is f32; both weight layouts give the same bits.  K, N, K2
+ * multiples of 8; f32 inputs, gate and up weights of different layouts or
+ * strides, or row-major ones whose K rows span 2^31 bytes or more give
+ * CHAIN_ERR_UNSUPPORTED.  Other conventions as chain_mlp_fwd.
  */
 chain_status chain_mlp_gated_fwd(const chain_tensor *X, const chain_tensor *Wg,
                                  const chain_tensor *Wu, const chain_tensor *Wd,

@@ -322,9 +322,18 @@ def test_mlp_gated_validation_codes(lib):
     assert call(w=None) == CODES["CHAIN_ERR_WORKSPACE"]
     assert call(n=need - 1) == CODES["CHAIN_ERR_WORKSPACE"]
     assert call(act=9, w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
-    # gate/up weights must be column-major with equal strides
+    # gate/up weights share one layout (row- or column-major) and their strides
     assert call(wg=td([256, 128], chain.BF16, FAKE + G), w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
     assert call(wu=td([256, 128], chain.BF16, FAKE + 2 * G, stride=[1, 272]), w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    rg, ru = td([256, 128], chain.BF16, FAKE + G), td([256, 128], chain.BF16, FAKE + 2 * G)
+    assert call(wg=rg, wu=ru, w=None) == CODES["CHAIN_ERR_WORKSPACE"]   # both row-major: valid
+    assert call(wg=rg, wu=td([256, 128], chain.BF16, FAKE + 2 * G, stride=[136, 1]),
+                w=None) == CODES["CHAIN_ERR_UNSUPPORTED"]
+    # row-major rows whose band passes 2^31 bytes (checked before any launch)
+    # (the two bands overlap each other, which inputs may, and end below O)
+    far = 2 ** 22 + 2 ** 16
+    assert call(wg=td([256, 128], chain.BF16, FAKE + G, stride=[far, 1]),
+                wu=td([256, 128], chain.BF16, FAKE + G + 1024, stride=[far, 1])) == CODES["CHAIN_ERR_UNSUPPORTED"]
     assert call(wu=td([256, 136], chain.BF16, FAKE + 2 * G, stride=[1, 264]), w=None) == CODES["CHAIN_ERR_SHAPE"]
     assert call(wd=td([128, 256], chain.F32, FAKE + 3 * G), w=None) == CODES["CHAIN_ERR_DTYPE"]
     f32 = dict(x=td([512, 256], chain.F32, FAKE), wg=td([256, 128], chain.F32, FAKE + G, stride=[1, 264]),

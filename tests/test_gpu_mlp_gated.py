@@ -90,6 +90,49 @@ def test_gated_mlp_down_weight_layouts_agree():
     assert torch.equal(a, b)
 
 
+def _gated_width(M, N, cus=256):
+    """The library's gated tile choice: 32 x nbw output columns, nbw 2 unless 4
+    takes no more rounds x nbw."""
+    def cost(nbw):
+        tiles = -(-M // 256) * -(-N // (32 * nbw))
+        return -(-tiles // cus) * nbw
+    return 2 if cost(2) < cost(4) else 4
+
+
+@pytest.mark.parametrize("M,K,N,K2,pad,nbw", [
+    (300, 256, 136, 264, 0, 2),      # last inner tile of 8 columns
+    (4096, 1376, 4096, 264, 0, 4),   # 128-wide tiles, whole stages
+    (4000, 264, 4000, 136, 0, 4),    # 128-wide tiles, ragged N, a K tail after eight stages
+    (96, 24, 40, 16, 0, 2),          # K inside one partial stage
+    (1000, 512, 392, 264, 24, 2),    # gate and up rows padded past N
+    (16384, 4096, 1376, 4096, 0, 4),  # the FFN shard
+])
+def test_gated_mlp_gate_up_layouts_agree(M, K, N, K2, pad, nbw):
+    """Row-major gate and up weights give the bits of column-major ones (the same
+    products in the same k order), and match the oracle on sampled rows."""
+    dev = device()
+    if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
+        pytest.skip("the tile choice asserted here assumes 256 compute units")
+    assert _gated_width(M, N) == nbw
+    x, wg, wu, wd = gen_mlp_gated(M, K, N, K2, amp_x=1.0, amp_w=0.02 if K > 512 else 0.05, seed=95 + M % 89)
+    announce(f"mlp_gated gate/up layouts M{M} K{K} N{N} K2{K2} pad {pad}")
+    xd, wdd = x.to(dev), wd.to(dev)
+
+    def rowmajor(w):
+        buf = torch.zeros(K, N + pad, dtype=w.dtype, device=dev)
+        buf[:, :N] = w.to(dev)
+        return buf[:, :N]
+    o_r = chain.mlp_gated_fwd(xd, rowmajor(wg), rowmajor(wu), wdd, act="silu")
+    o_k = chain.mlp_gated_fwd(xd, _kmajor(wg.to(dev)), _kmajor(wu.to(dev)), wdd, act="silu")
+    torch.cuda.synchronize()
+    assert torch.equal(o_r, o_k)
+    rows = sample_rows(M, 48, 95, extra=(0, M - 1, min(M - 1, 255), min(M - 1, 256)))
+    ref = oracle.mlp_gated(f64(x[rows]), f64(wg), f64(wu), f64(wd), "silu")
+    err = max_abs(f64(o_r.cpu()[rows]), ref)
+    print(f"max-abs {err:.3e} over {len(rows)} rows")
+    assert err <= TOL_BF16
+
+
 def test_gated_mlp_shard_sum_equals_whole():
     """Inner-dimension shards of gate, up and down summed give the unsharded chain
     (f32 output: the bf16 intermediate is rounded element by element either way)."""
