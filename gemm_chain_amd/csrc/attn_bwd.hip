@@ -269,13 +269,13 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
     };
     auto compute = [&](int kt, int st) {
       const int k0 = kt * BN;
-      if (!wave_rows || (p.causal && k0 > w_qmax)) return;
+      if (__builtin_expect(!wave_rows || (p.causal && k0 > w_qmax), 0)) return;
       const char *sb = lds + st * SB;
       const bool full = k0 + BN <= p.S && (!p.causal || k0 + BN - 1 <= row0);
       const int lim = p.causal ? min(p.S - 1, my_row) : p.S - 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (p.causal && k0 + 32 * kb > w_qmax) continue;
+        if (__builtin_expect(p.causal && k0 + 32 * kb > w_qmax, 0)) continue;
         const char *kt_ = sb + kb * 32 * RB;
         f32x16 s, dp = f32x16{};
         run_b128<KS>([&](int i) { return kt_ + fo.aoff[i]; },
@@ -285,7 +285,7 @@ __device__ __forceinline__ void dq_body(const AttnBwdParams &p) {
         // lane (h2, l32) holds key k0 + 32kb + 8(r/4) + 4h2 + r%4 of query my_row;
         // keys past the limit get score -inf, so probability 0 (a uniform
         // branch: full tiles skip the compares)
-        if (!full) {
+        if (__builtin_expect(!full, 0)) {
           const int rel = lim - (k0 + 32 * kb + 4 * h2);
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = 8 * (r >> 2) + (r & 3) <= rel ? s[r] : -INFINITY;
@@ -429,9 +429,9 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
                                                  t * QT * 8 + 128 * wave + 16 * lane, 0, 0, 0);
     };
     auto compute = [&](int st_i, int st) {
-      if (!wave_keys) return;
+      if (__builtin_expect(!wave_keys, 0)) return;
       const int q0 = (t0 + st_i % per_head) * QT;
-      if (p.causal && q0 + QT - 1 < kw0) return;   // every query precedes every key
+      if (__builtin_expect(p.causal && q0 + QT - 1 < kw0, 0)) return;   // every query precedes every key
       const char *sb = lds + st * SB;
       const float *rv = (const float *)(sb + 2 * TB);
       // query q0 + 32qb + 8g + 4h2 + e sees key my_key iff 32qb + 8g + e >= qoff
@@ -452,7 +452,7 @@ __device__ __forceinline__ void dkdv_body(const AttnBwdParams &p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) sinit[qb][4 * g + e] = l4[e], dpinit[qb][4 * g + e] = d4[e];
         }
-      if (p.causal && q0 < kw0 + 31) {
+      if (__builtin_expect(p.causal && q0 < kw0 + 31, 0)) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll

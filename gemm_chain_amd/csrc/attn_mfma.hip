@@ -32,7 +32,10 @@
 // bank groups.  Inside each MFMA run the LDS fragments are read kAhead MFMAs
 // ahead of use (pinned with scheduling barriers); the first ones of a K.Q^T run
 // are read at the end of the softmax phase before it.  Scalar branches cost
-// tens of cycles even when not taken, so the tile loop keeps them few.
+// tens of cycles even when not taken (about twice that when taken), so the
+// tile loop keeps them few and marks the rare paths (masked tiles, the slow
+// softmax path, range switches, V tails) unlikely, so that the common path
+// falls through every branch.
 //
 // Q is multiplied by scale * log2(e) and rounded to bf16 once per query tile,
 // and each K.Q^T accumulator starts from minus the row's reference max m, so
@@ -212,7 +215,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     a.k0 += BN;
     b.k0 += BN;
     c.k0 += BN;
-    if ((a.k0 >= a.stop) | (b.k0 >= b.stop) | (c.k0 >= c.stop)) {
+    if (__builtin_expect((a.k0 >= a.stop) | (b.k0 >= b.stop) | (c.k0 >= c.stop), 0)) {
       if (a.k0 >= a.stop) a = seek(a.ri + 1);
       if (b.k0 >= b.stop) b = seek(b.ri + 1);
       if (c.k0 >= c.stop) c = seek(c.ri + 1);
@@ -243,7 +246,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   // V rows past a range end are cleared once this wave's own loads of them
   // have landed, so that a masked key multiplies zeros whatever the input holds.
   auto zero_v_tail = [&](const It &x, char *stage) {
-    if ((grp == 1) & valid(x) & (x.k0 + BN > x.kend)) {
+    if (__builtin_expect((grp == 1) & valid(x) & (x.k0 + BN > x.kend), 0)) {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int q = 0; q < LO; ++q)
@@ -377,7 +380,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     // operand of the next P.V run), the row sum l and the lazily raised
     // reference max m.
     auto softmax = [&](const It &x, int cls) {
-      if (cls == TILE_DIAG) {
+      if (__builtin_expect(cls == TILE_DIAG, 0)) {
         // key of register r in lane half h2 is kb*32 + 8*(r/4) + 4*h2 + r%4: compare
         // its compile-time part with per-lane limits (branch-free selects)
         const int nvalid = min(BN, x.kend - x.k0);
@@ -406,7 +409,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
           rs += e;
           pk[kb][r >> 3][r & 7] = (__bf16)e;
         }
-      if (__any(!(rs <= kLaneSumMax)) | !ref_ready) {
+      if (__builtin_expect(__any(!(rs <= kLaneSumMax)) | !ref_ready, 0)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -482,8 +485,8 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         const char *ks = kring + ST * TB;
         const char *vs = vring + ((ST + NST - 1) % NST) * TB;
         __builtin_amdgcn_s_setprio(1);
-        if (cls != TILE_SKIP) mfma_run(QK{}, NONE{}, ks, vs, std::true_type{}, [](int) {});
-        if (prev_live) mfma_run(NONE{}, PV{}, ks, vs, std::false_type{}, [](int) {});
+        if (__builtin_expect(cls != TILE_SKIP, 1)) mfma_run(QK{}, NONE{}, ks, vs, std::true_type{}, [](int) {});
+        if (__builtin_expect(prev_live, 1)) mfma_run(NONE{}, PV{}, ks, vs, std::false_type{}, [](int) {});
         __builtin_amdgcn_s_setprio(0);
         wait_vmcnt<LO>();   // all but the loads of this wave's latest S step
         zero_v_tail(cur, vring + ST * TB);
@@ -495,7 +498,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         constexpr int ST = decltype(st_c)::value;
         const It &ld = grp == 0 ? (valid(itk) ? itk : first) : (valid(itv) ? itv : first);
         issue(ld, grp == 0 ? kring + ((ST + 3) % NST) * TB : vring + ((ST + 2) % NST) * TB);
-        if (cls != TILE_SKIP) softmax(cur, cls);
+        if (__builtin_expect(cls != TILE_SKIP, 1)) softmax(cur, cls);
         prev_live = cls != TILE_SKIP;
         step3(cur, itv, itk);
         cls = tile_class(cur);
