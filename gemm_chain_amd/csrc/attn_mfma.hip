@@ -190,43 +190,68 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   bool wave_rows = false, row_ok = false;
   bf16x8 qraw[KS], qf[KS];
 
-  // ---- tile iterators (uniform over the workgroup).  Tiles of BN keys are
-  // cut inside each key range, up to the last key position this tile's
-  // queries can see (stop); n counts them.  Stepping within a range is one
-  // add and one compare; the range switch is rare.  Scalar branches cost tens
-  // of cycles even when not taken, so the three iterators of the loop step
-  // together behind one branch.
-  struct It { int ri, k0, stop, kend, off; };   // ri == p.kr.n: past the last tile
+  // ---- tile iterators (wave-uniform).  Tiles of BN keys are cut inside each
+  // key range, up to the last key position this tile's queries can see (stop);
+  // n counts them.  Each wave steps two iterators: cur (the tile it computes)
+  // and ld (the tile whose K, group 0, or V, group 1, it loads next).  All that
+  // a step needs is precomputed when an iterator enters a range (rare), so a
+  // step within a range is a few scalar adds and compares behind one branch:
+  //   kskip, kdiag: a tile from k0 >= kskip on is skipped by this wave, from
+  //     k0 >= kdiag on masked (the causal diagonal or the range's ragged end);
+  //   kzt: from k0 >= kzt on, group 1 clears V rows past the range end;
+  //   base, rem: the buffer descriptor of the tile's own-operand rows (its
+  //     first row, and the bytes up to the range end), advanced by dstep;
+  //   left: tiles of the range after this one (the range switch when < 0).
+  // Past the last tile ld repeats the first tile (dstep 0) and cur is skipped.
+  struct It {
+    int ri, k0, left, kend, off;   // ri == p.kr.n: past the last tile
+    int kskip, kdiag, kzt;
+    const char *base;
+    int rem, dstep;
+  };
+  It first{}, cur{}, ld{};
   auto range_stop = [&](int r) {
     return p.causal ? min(p.kr.end[r], wg_qmax - p.kr.pos_off[r] + 1) : p.kr.end[r];
   };
   auto seek = [&](int r) -> It {   // first tile of the first live range at or after r
     for (; r < p.kr.n; ++r) {
       const int st = range_stop(r);
-      if (st > p.kr.beg[r]) return It{r, p.kr.beg[r], st, p.kr.end[r], p.kr.pos_off[r]};
+      const int k0 = p.kr.beg[r], kend = p.kr.end[r], off = p.kr.pos_off[r];
+      if (st > k0) {
+        // classify_tile's tests as thresholds on k0: skipped once the first key
+        // passes the wave's last query; masked once the last key passes its
+        // first query, or the tile is cut short by the range end
+        const int kskip = !wave_rows ? INT_MIN : p.causal ? w_qmax - off + 1 : INT_MAX;
+        const int kdiag = min(kend - BN + 1, p.causal ? w_qmin - off - BN + 2 : INT_MAX);
+        return It{r, k0, (st - k0 - 1) / BN, kend, off, kskip, kdiag, grp == 1 ? kend - BN + 1 : INT_MAX,
+                  own_b8 + (uint32_t)k0 * own_ss2, (int)((uint32_t)(kend - k0 - 1) * own_ss2 + 2 * D),
+                  (int)((uint32_t)BN * own_ss2)};
+      }
     }
-    return It{p.kr.n, 0, INT_MAX, 0, 0};   // never steps into a range switch
+    return It{p.kr.n, 0, INT_MAX, 0, 0, INT_MIN, INT_MIN, INT_MAX, first.base, first.rem, 0};   // never switches
   };
-  auto step = [&](It &x) {
-    x.k0 += BN;
-    if (x.k0 >= x.stop) x = seek(x.ri + 1);
+  auto step_ld = [&](It &l) {
+    l.left -= 1;
+    l.base += (uint32_t)l.dstep;
+    l.rem -= l.dstep;
   };
-  auto step3 = [&](It &a, It &b, It &c) {
-    a.k0 += BN;
-    b.k0 += BN;
+  auto step_one = [&](It &x) {
+    step_ld(x);
+    if (x.left < 0) x = seek(x.ri + 1);
+  };
+  auto step2 = [&](It &c, It &l) {
     c.k0 += BN;
-    if (__builtin_expect((a.k0 >= a.stop) | (b.k0 >= b.stop) | (c.k0 >= c.stop), 0)) {
-      if (a.k0 >= a.stop) a = seek(a.ri + 1);
-      if (b.k0 >= b.stop) b = seek(b.ri + 1);
-      if (c.k0 >= c.stop) c = seek(c.ri + 1);
+    c.left -= 1;
+    step_ld(l);
+    if (__builtin_expect(min(c.left, l.left) < 0, 0)) {
+      if (c.left < 0) c = seek(c.ri + 1);
+      if (l.left < 0) l = seek(l.ri + 1);
     }
   };
-  auto valid = [&](const It &x) { return x.ri < p.kr.n; };
-  // What this wave does with a tile: skip it, take it whole, or mask it.
+  // What this wave does with a tile: skip it, take it whole, or mask it (the
+  // tests of classify_tile, precomputed as thresholds).
   auto tile_class = [&](const It &x) -> int {
-    const int nvalid = min(BN, x.kend - x.k0);
-    const int c = classify_tile(p.causal, w_qmin, w_qmax, x.k0 + x.off, x.k0 + nvalid - 1 + x.off, nvalid < BN);
-    return (valid(x) & wave_rows) ? c : TILE_SKIP;
+    return x.k0 >= x.kskip ? TILE_SKIP : x.k0 >= x.kdiag ? TILE_DIAG : TILE_FULL;
   };
   // Direct-to-LDS loads of one operand of one tile into a ring stage: each
   // wave-level load puts 64 lanes x 16 bytes (RPL key rows) into LDS.  The
@@ -235,9 +260,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   // short: keys past the range end are out of the buffer and read as zero
   // (their scores are masked, their V rows cleared as well).
   auto issue = [&](const It &x, char *stage) {   // this wave's part of its group's operand
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(own_b8 + (uint32_t)x.k0 * own_ss2), 0, (int)((uint32_t)(x.kend - x.k0 - 1) * own_ss2 + 2 * D),
-        0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)x.base, 0, x.rem, 0x00020000);
 #pragma unroll
     for (int q = 0; q < LO; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(stage + (w4 * LO + q) * 1024),
@@ -246,7 +269,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
   // V rows past a range end are cleared once this wave's own loads of them
   // have landed, so that a masked key multiplies zeros whatever the input holds.
   auto zero_v_tail = [&](const It &x, char *stage) {
-    if (__builtin_expect((grp == 1) & valid(x) & (x.k0 + BN > x.kend), 0)) {
+    if (__builtin_expect(x.k0 >= x.kzt, 0)) {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int q = 0; q < LO; ++q)
@@ -254,7 +277,6 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       wait_lgkmcnt0();
     }
   };
-  It first{}, cur{}, itv{}, itk{};
 
   auto set_pass = [&](int t) {
     const int wg_row0 = t * ROWS;
@@ -289,23 +311,24 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       for (int e = 0; e < 8; ++e) qf[ks][e] = row_ok ? (__bf16)((float)qraw[ks][e] * c) : (__bf16)0.f;
   };
   // The ring's first loads of a pass: group 0 K of tiles 0, 1 and 2, group 1
-  // V of tiles 0 and 1.  cur: tile j (K.Q^T, softmax); itv: tile j+2 and itk:
-  // tile j+3, whose V and K are loaded in S_j.  Past the last tile the loads
-  // repeat the first tile into the free stages, so every step has the same
-  // loads in flight.
+  // V of tiles 0 and 1.  cur: tile j (K.Q^T, softmax); ld: tile j+3 (group 0)
+  // or j+2 (group 1), whose K or V is loaded in S_j.  Past the last tile the
+  // loads repeat the first tile into the free stages, so every step has the
+  // same loads in flight.
   char *const own_ring = grp == 0 ? kring : vring;
   auto start_tiles = [&] {
     if (n > 0) {
       first = seek(0);
       cur = first;
-      itv = first;
-      step(itv);
-      issue(cur, own_ring);
-      issue(valid(itv) ? itv : first, own_ring + TB);
-      step(itv);
-      itk = itv;
-      if (grp == 0) issue(valid(itk) ? itk : first, kring + 2 * TB);
-      step(itk);
+      ld = first;
+      issue(ld, own_ring);
+      step_one(ld);
+      issue(ld, own_ring + TB);
+      step_one(ld);
+      if (grp == 0) {
+        issue(ld, kring + 2 * TB);
+        step_one(ld);
+      }
     }
   };
 
@@ -324,7 +347,9 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     // scores minus the reference and the fast path's probability is one exp2.
     float m = -INFINITY, l = 0.f, mu = 0.f;
     f32x16 mref = f32x16{};   // -mu in every element
-    bool ref_ready = false;   // every lane of the wave holds a finite reference max
+    // the fast path's lane-sum bound: kLaneSumMax once every lane of the wave
+    // holds a finite reference max, -1 (no lane passes) before that
+    float sum_bound = -1.f;
     f32x16 s[2];
     bf16x8 pk[2][2];
 
@@ -409,7 +434,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
           rs += e;
           pk[kb][r >> 3][r & 7] = (__bf16)e;
         }
-      if (__builtin_expect(__any(!(rs <= kLaneSumMax)) | !ref_ready, 0)) {
+      if (__builtin_expect(__any(!(rs <= sum_bound)), 0)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -440,7 +465,7 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
             rs += e;
             pk[kb][r >> 3][r & 7] = (__bf16)e;
           }
-        ref_ready = !__any(m == -INFINITY);
+        sum_bound = __any(m == -INFINITY) ? -1.f : kLaneSumMax;
       }
       l += rs;
     };
@@ -496,11 +521,10 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       // the end, the first K fragments of C_j+1
       auto softmax_step = [&](auto st_c) {
         constexpr int ST = decltype(st_c)::value;
-        const It &ld = grp == 0 ? (valid(itk) ? itk : first) : (valid(itv) ? itv : first);
         issue(ld, grp == 0 ? kring + ((ST + 3) % NST) * TB : vring + ((ST + 2) % NST) * TB);
         if (__builtin_expect(cls != TILE_SKIP, 1)) softmax(cur, cls);
         prev_live = cls != TILE_SKIP;
-        step3(cur, itv, itk);
+        step2(cur, ld);
         cls = tile_class(cur);
         early(kring + ((ST + 1) % NST) * TB);
       };
