@@ -193,6 +193,27 @@ def test_mlp_row_stride_beyond_32bit_tile_offsets():
     del store, xs
 
 
+def test_mlp_row_major_weight_stride_beyond_32bit_offsets():
+    """Row-major W2 rows 20 M elements apart: its column band spans more than 2^31
+    bytes, so H.W2 runs on the register-staged kernel (64-bit addresses) instead of
+    the direct-to-LDS one; the same k order gives the contiguous call's bits."""
+    dev = device()
+    M, K, N, K2, ldb = 300, 128, 136, 96, 20_000_000
+    x, w1, w2 = gen_mlp(M, K, N, K2, dtype="bf16", amp_x=1.0, amp_w=0.05, seed=76)
+    xd, w1d, w2d = x.to(dev), w1.to(dev), w2.to(dev)
+    announce(f"mlp row-major W2 row stride {ldb} (band beyond 2^31 bytes)")
+    store = torch.zeros((N - 1) * ldb + K2, dtype=torch.bfloat16, device=dev)
+    w2s = store.as_strided((N, K2), (ldb, 1))
+    w2s.copy_(w2d)
+    o = chain.mlp_fwd(xd, w1d, w2s, act="gelu_erf")
+    dense = chain.mlp_fwd(xd, w1d, w2d, act="gelu_erf")
+    torch.cuda.synchronize()
+    assert torch.equal(o, dense)
+    ref = oracle.mlp(f64(x), f64(w1), f64(w2), "gelu_erf")
+    assert max_abs(f64(o), ref) <= TOL_BF16
+    del store, w2s
+
+
 @pytest.mark.parametrize("w2_kmajor", [False, True])
 @pytest.mark.parametrize("pad", [2, 4])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
