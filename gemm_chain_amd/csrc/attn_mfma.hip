@@ -26,16 +26,16 @@
 // Tiles reach LDS by buffer loads that write LDS directly (64 lanes x 16 bytes
 // per wave-level load, no staging registers, no LDS write instructions) into a
 // K ring and a V ring of four stages each: at the start of softmax phase j,
-// waves 0-3 issue all of tile j+3's K and waves 4-7 all of tile j+2's V.
+// waves 0-3 issue all of tile j+3's K and waves 4-7 all of tile j+3's V.
 // Staged rows are not padded: 16-byte chunks are XOR-swizzled per row so that
 // the 16-byte K fragment reads and the transposing V reads each hit distinct
 // bank groups.  Inside each MFMA run the LDS fragments are read kAhead MFMAs
-// ahead of use (pinned with scheduling barriers); the first ones of a K.Q^T run
-// are read at the end of the softmax phase before it.  Scalar branches cost
-// tens of cycles even when not taken (about twice that when taken), so the
-// tile loop keeps them few and marks the rare paths (masked tiles, the slow
-// softmax path, range switches, V tails) unlikely, so that the common path
-// falls through every branch.
+// ahead of use (pinned with scheduling barriers); the first ones of both runs
+// of a phase are read at the end of the softmax phase before it.  Scalar
+// branches cost tens of cycles even when not taken (about twice that when
+// taken), so the tile loop keeps them few and marks the rare paths (masked
+// tiles, the slow softmax path, range switches, V tails) unlikely, so that the
+// common path falls through every branch.
 //
 // Q is multiplied by scale * log2(e) and rounded to bf16 once per query tile,
 // and each K.Q^T accumulator starts from minus the row's reference max m, so
@@ -310,11 +310,10 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[ks][e] = row_ok ? (__bf16)((float)qraw[ks][e] * c) : (__bf16)0.f;
   };
-  // The ring's first loads of a pass: group 0 K of tiles 0, 1 and 2, group 1
-  // V of tiles 0 and 1.  cur: tile j (K.Q^T, softmax); ld: tile j+3 (group 0)
-  // or j+2 (group 1), whose K or V is loaded in S_j.  Past the last tile the
-  // loads repeat the first tile into the free stages, so every step has the
-  // same loads in flight.
+  // The ring's first loads of a pass: group 0 K, group 1 V of tiles 0, 1 and
+  // 2.  cur: tile j (K.Q^T, softmax); ld: tile j+3, whose K or V is loaded in
+  // S_j.  Past the last tile the loads repeat the first tile into the free
+  // stages, so every step has the same loads in flight.
   char *const own_ring = grp == 0 ? kring : vring;
   auto start_tiles = [&] {
     if (n > 0) {
@@ -325,10 +324,8 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       step_one(ld);
       issue(ld, own_ring + TB);
       step_one(ld);
-      if (grp == 0) {
-        issue(ld, kring + 2 * TB);
-        step_one(ld);
-      }
+      issue(ld, own_ring + 2 * TB);
+      step_one(ld);
     }
   };
 
@@ -355,34 +352,36 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
 
     // MFMA run: NQ products of S^T = K.Q^T on a K stage, then NP products of
     // O^T += V^T.P^T on a V stage (the previous tile's P).  LDS fragments are
-    // read kAhead MFMAs ahead of use; a K.Q^T run may take its first ones from
-    // fq (pre).
-    // The first kAhead K fragments of a K.Q^T run (pre = true) come from fq,
-    // read at the end of the softmax step before it, so their LDS latency passes
-    // under the barrier.
-    bf16x8 fq[kAhead];
+    // read kAhead MFMAs ahead of use.  With pre = true a run takes its first
+    // kAhead fragments from fq (a K.Q^T run) or fv (a P.V run), read at the end
+    // of the softmax step before it, so their LDS latency passes under the
+    // barrier and (for fv) under the K.Q^T run.
+    bf16x8 fq[kAhead], fv[kAhead];
     auto kfrag = [&](const char *ks, int i) -> bf16x8 {
       return *(const bf16x8 *)(ks + koff[i >> 1] + (i & 1) * 32 * RB);
+    };
+    auto vfrag = [&](const char *vs, int k) -> bf16x8 {
+      const __bf16 *a = (const __bf16 *)(vs + voff[k >> 2] + (((k >> 1) & 1) * 32 + 16 * (k & 1)) * RB);
+      const i16x4 lo = ds_read_tr(a), hi = ds_read_tr(a + 8 * D);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto early = [&](const char *ks) {
 #pragma unroll
       for (int i = 0; i < kAhead; ++i) fq[i] = kfrag(ks, i);
     };
+    auto early_v = [&](const char *vs) {
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) fv[i] = vfrag(vs, i);
+    };
     auto mfma_run = [&](auto nq_c, auto np_c, const char *ks, const char *vs, auto pre_c, auto hook) {
       constexpr int NQ = decltype(nq_c)::value, NP = decltype(np_c)::value, N = NQ + NP;
       constexpr bool PRE = decltype(pre_c)::value;
-      static_assert(!PRE || NQ >= kAhead, "preloaded fragments are K fragments");
-      auto frag = [&](int i) -> bf16x8 {
-        if (i < NQ) return kfrag(ks, i);
-        const int k = i - NQ;
-        const __bf16 *a = (const __bf16 *)(vs + voff[k >> 2] + (((k >> 1) & 1) * 32 + 16 * (k & 1)) * RB);
-        const i16x4 lo = ds_read_tr(a), hi = ds_read_tr(a + 8 * D);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
+      static_assert(!PRE || (NQ == 0 ? NP : NQ) >= kAhead, "preloaded fragments of one operand");
+      auto frag = [&](int i) -> bf16x8 { return i < NQ ? kfrag(ks, i) : vfrag(vs, i - NQ); };
       bf16x8 f[kAhead];
 #pragma unroll
       for (int i = 0; i < kAhead; ++i)
-        if (i < N) f[i] = PRE ? fq[i] : frag(i);
+        if (i < N) f[i] = PRE ? (NQ > 0 ? fq[i] : fv[i]) : frag(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < N; ++i) {
@@ -484,20 +483,23 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
     //
     // Tile j's K sits in K stage j%4 and is read in phases 2j and 2j+1 (its
     // first fragments at the end of phases 2j-1 and 2j); its V sits in V stage
-    // j%4 and is read in phases 2j+2 and 2j+3.  In S_j group 0 issues all of
-    // tile j+3's K (phase 2j+1) and group 1 all of tile j+2's V (phase 2j+2),
-    // into stages last read in phase 2j-1.  Past the last tile the free stages
-    // are refilled with tile j, so every step has the same loads in flight.
-    // Each wave issues LO loads per S step (group 0: K0 K1 K2 | K3 | K4 | ...,
-    // group 1: V0 V1 | V2 | V3 | ...) and waits at the end of each C step for
-    // all but those of its latest S step: at the end of C_j (phase 2j for group
-    // 0, 2j+1 for group 1) K of tile j+1, resp. V of tile j, has landed, issued
-    // three phases earlier, and the barrier that follows publishes it before the
-    // first fragment reads of C_j+1.
+    // j%4 and is read in phases 2j+1 to 2j+3 (its first fragments at the end of
+    // S_j, phases 2j+1 and 2j+2; the P.V runs of C_j+1 in 2j+2 and 2j+3).  In
+    // S_j group 0 issues all of tile j+3's K (phase 2j+1) and group 1 all of
+    // tile j+3's V (phase 2j+2), into stages last read in phase 2j+1.  Past the
+    // last tile the free stages are refilled with tile j, so every step has the
+    // same loads in flight.  Each wave issues LO loads per S step (K0 K1 K2 |
+    // K3 | K4 | ..., V0 V1 V2 | V3 | ...) and waits at the end of each C step
+    // for all but those of its latest S step: at the end of C_j (phase 2j for
+    // group 0, 2j+1 for group 1) K, resp. V, of tile j+1 has landed, issued
+    // three phases earlier, and the barrier that follows publishes it.  Group 1
+    // clears the V rows of tile j+1 past a range end in S_j (phase 2j+2),
+    // published before group 0's first reads of them (phase 2j+3).
     if (n > 0) {
       // K of tile 0 has landed (pass 1: all its first loads landed before the
       // previous pass's outputs were stored, and the stores must not be waited on)
-      if (pass == 0) wait_vmcnt<2 * LO>();   // group 0: K of tile 0 (group 1: no wait)
+      if (pass == 0) wait_vmcnt<2 * LO>();   // K, resp. V, of tile 0
+      zero_v_tail(cur, vring);
       barrier();
       early(kring);
       int cls = tile_class(cur);
@@ -511,22 +513,24 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
         const char *vs = vring + ((ST + NST - 1) % NST) * TB;
         __builtin_amdgcn_s_setprio(1);
         if (__builtin_expect(cls != TILE_SKIP, 1)) mfma_run(QK{}, NONE{}, ks, vs, std::true_type{}, [](int) {});
-        if (__builtin_expect(prev_live, 1)) mfma_run(NONE{}, PV{}, ks, vs, std::false_type{}, [](int) {});
+        if (__builtin_expect(prev_live, 1)) mfma_run(NONE{}, PV{}, ks, vs, std::true_type{}, [](int) {});
         __builtin_amdgcn_s_setprio(0);
         wait_vmcnt<LO>();   // all but the loads of this wave's latest S step
-        zero_v_tail(cur, vring + ST * TB);
       };
-      // S_j: this wave's part of tile j+3's K (group 0) or tile j+2's V (group 1)
-      // goes out first, so that the loads are in flight during the softmax; at
-      // the end, the first K fragments of C_j+1
+      // S_j: this wave's part of tile j+3's K (group 0) or V (group 1) goes out
+      // first, so that the loads are in flight during the softmax; group 1 then
+      // clears tile j+1's V tail, and at the end each wave reads the first K
+      // fragments of C_j+1's K.Q^T run and the first V fragments of its P.V run
       auto softmax_step = [&](auto st_c) {
         constexpr int ST = decltype(st_c)::value;
-        issue(ld, grp == 0 ? kring + ((ST + 3) % NST) * TB : vring + ((ST + 2) % NST) * TB);
+        issue(ld, own_ring + ((ST + 3) % NST) * TB);
         if (__builtin_expect(cls != TILE_SKIP, 1)) softmax(cur, cls);
         prev_live = cls != TILE_SKIP;
         step2(cur, ld);
         cls = tile_class(cur);
+        zero_v_tail(cur, vring + ((ST + 1) % NST) * TB);
         early(kring + ((ST + 1) % NST) * TB);
+        early_v(vring + ST * TB);
       };
       using St0 = std::integral_constant<int, 0>;
       using St1 = std::integral_constant<int, 1>;
