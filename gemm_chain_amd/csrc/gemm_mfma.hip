@@ -868,29 +868,45 @@ CHAIN_W8_KERNELS(silu, CHAIN_ACT_SILU)
 // it also beats a double-buffered k-step by about 1 % at 256): each is read
 // PD MFMAs before its first use, and the stage's wait and barrier sit PD MFMAs
 // before its end, after the last read of the stage and before the reads of the
-// next.  Ring, stage depth, swizzle, descriptors and k order are those of the
-// gated and four-wave kernels, so all give the same bits.
+// next.  The k order is that of the gated and four-wave kernels, so all give
+// the same bits.
+//
+// Stage depth SD: 32 k in a ring of four stages (three in flight), or 64 k in
+// a ring of two (one in flight).  With 64 a k-major row of a stage is 128
+// bytes, so each row's request to the L2 is a whole 128-byte line where 32
+// takes half a line per stage (and the other half again a stage later): about
+// 30 % fewer L2 requests for the same bytes.  Two stages in flight less hide
+// the load latency only where a stage has enough MFMAs, so 64 serves the 256-
+// and 352-wide tiles and 32 the narrower ones.
 //
 // BKM false takes B row-major ([K, N], n contiguous): load q of a wave then
-// covers 64 consecutive 16-byte chunks of the stage's 32 x BN block in row
+// covers 64 consecutive 16-byte chunks of the stage's SD x BN block in row
 // order, and a B fragment is two ds_read_b64_tr_b16 of four k rows.  A
 // transposing read takes 64 bytes (a 64-byte group) of each of four
 // consecutive rows; the groups of row r are XOR-swizzled by row_swz(r) so that
 // the four land on disjoint banks (at 352 columns the 704-byte pitch already
 // does that).
-template <int NB0, int NB1, int ACT, bool BKM = true>
+template <int NB0, int NB1, int ACT, bool BKM = true, int SD = DBK>
 __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   constexpr int BN = 32 * (NB0 + NB1);
+  // SD: k per stage, 32 (a ring of four stages) or 64 (two).  A k-major row
+  // of a stage is SD / 8 16-byte chunks, RPL rows per 1 KB load; chunk c of
+  // row r sits at c ^ kswz(r), so that the 16-byte fragment reads of 16
+  // consecutive rows hit 16 distinct bank groups.
+  static_assert(SD == 32 || SD == 64, "stage depth");
+  constexpr int NS = SD == 32 ? 4 : 2;
+  constexpr int CPR = SD / 8, RPL = 64 / CPR, RBY = 2 * SD;
+  auto kswz = [](int r) { return SD == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
   constexpr int BCH = BN / 8, BG = BN / 32;     // 16-byte chunks, 64-byte groups per row-major B row
   // Pitch 64 BG bytes: rows r..r+3 start 16 BG banks apart.  BG = 0 mod 4: all
   // on one bank group, swizzle by r & 3; BG = 2 mod 4: two apart, by (r >> 1) & 1.
   auto row_swz = [](int r) { return BG % 4 == 0 ? (r & 3) : BG % 4 == 2 ? ((r >> 1) & 1) : 0; };
-  constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
-  static_assert(DST * STAGE <= 160 * 1024, "the ring must fit in LDS");
-  constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
-  constexpr int LA = BM / 16 / 8;               // 1 KB loads of A per wave and stage
+  constexpr int A_BYTES = BM * SD * 2, B_BYTES = BN * SD * 2, STAGE = A_BYTES + B_BYTES;
+  static_assert(NS * STAGE <= 160 * 1024, "the ring must fit in LDS");
+  constexpr int NLB = B_BYTES / 1024;           // 1 KB loads of B per stage
+  constexpr int LA = A_BYTES / 1024 / 8;        // 1 KB loads of A per wave and stage
   constexpr int LBH = (NLB + 7) / 8, LBL = NLB / 8;   // of B: waves below NLB % 8 take LBH
-  __shared__ __attribute__((aligned(1024))) char lds[DST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
@@ -913,13 +929,14 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
                                               (int)(((int64_t)(rb - 1) * p.b_sn + p.K) * 2), 0x00020000)
           : __builtin_amdgcn_make_buffer_rsrc((void *)((const __bf16 *)p.b + n0), 0,
                                               (int)(((int64_t)(p.K - 1) * p.b_sk + rb) * 2), 0x00020000);
-  // Lane i of a load fetches row i >> 2 of its 16-row group, logical chunk lc;
-  // load q of a wave covers the 16-row group wave + 8 q of its operand.
-  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  // Lane i of a k-major load fetches row i / CPR of its RPL-row group, logical
+  // chunk lc; load q of a wave covers the group wave + 8 q of its operand (the
+  // swizzle of those rows depends on the group only through the wave's parity).
+  const int lc = (lane % CPR) ^ kswz(RPL * wave + lane / CPR);
   uint32_t aoff[LA], boff[LBH];
 #pragma unroll
   for (int q = 0; q < LA; ++q)
-    aoff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
+    aoff[q] = (uint32_t)min(RPL * (wave + 8 * q) + lane / CPR, ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
   // Row-major B: chunk 64 (wave + 8 q) + lane of a stage is row brow(q), columns
   // bcol(q) .. + 7 (past the tile's last column: its last chunk again).
   auto brow = [&](int q) { return (64 * (wave + 8 * q) + lane) / BCH; };
@@ -929,19 +946,19 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
   };
 #pragma unroll
   for (int q = 0; q < LBH; ++q)
-    boff[q] = BKM ? (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc
+    boff[q] = BKM ? (uint32_t)min(RPL * (wave + 8 * q) + lane / CPR, rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc
                   : (uint32_t)brow(q) * (uint32_t)p.b_sk * 2u + 2u * (uint32_t)bcol(q);
-  const int nk = (p.K + DBK - 1) / DBK;
+  const int nk = (p.K + SD - 1) / SD;
   typedef __attribute__((address_space(3))) void lds_void;
 
-  // Load q of this wave for stage kt (q < LA: A, else B) into ring slot kt % DST;
+  // Load q of this wave for stage kt (q < LA: A, else B) into ring slot kt % NS;
   // past the last stage, stage 0 again into a slot nobody reads.  Whole stages
   // carry the k offset in the scalar offset; in the K tail a chunk past K
   // fetches k = K - 8 of its row instead.
   auto issue_one = [&](int kt, int q, auto whole_c) {
-    char *sb = lds + (kt & (DST - 1)) * STAGE;
-    const int k0 = kt < nk ? kt * DBK : 0;
-    const bool whole = decltype(whole_c)::value || k0 + DBK <= p.K;
+    char *sb = lds + (kt & (NS - 1)) * STAGE;
+    const int k0 = kt < nk ? kt * SD : 0;
+    const bool whole = decltype(whole_c)::value || k0 + SD <= p.K;
     const uint32_t kv = whole ? 0u : 2u * (uint32_t)min(k0 + 8 * lc, p.K - 8) - 16u * lc;
     const int ks = whole ? 2 * k0 : 0;
     if (q < LA) {
@@ -962,9 +979,9 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
     }
   };
   auto zero_tail = [&](int kt) {   // after stage kt (the K tail) has landed
-    char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
+    char *sb = lds + (kt & (NS - 1)) * STAGE + lane * 16;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    if (kt * DBK + 8 * lc >= p.K) {
+    if (kt * SD + 8 * lc >= p.K) {
 #pragma unroll
       for (int q = 0; q < LA; ++q) *(u32x4 *)(sb + (wave + 8 * q) * 1024) = z;
       if constexpr (BKM) {
@@ -976,28 +993,30 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
     if constexpr (!BKM) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
-        if ((q < LBL || hi) && kt * DBK + brow(q) >= p.K) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+        if ((q < LBL || hi) && kt * SD + brow(q) >= p.K) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
     }
   };
-  // this wave's loads of the oldest stage in flight have landed (the two
+  // this wave's loads of the oldest stage in flight have landed (the NS - 2
   // stages after it may still be in flight)
   auto wait_landed = [&]() {
-    if (hi) wait_vmcnt<2 * (LA + LBH)>();
-    else wait_vmcnt<2 * (LA + LBL)>();
+    if (hi) wait_vmcnt<(NS - 2) * (LA + LBH)>();
+    else wait_vmcnt<(NS - 2) * (LA + LBL)>();
   };
 
-  const int sx = (l32 >> 2) & 3;
-  const int pc[2] = {(h2 ^ sx) * 16, ((2 + h2) ^ sx) * 16};
-  const int rowa = (wm * 64 + l32) * 64;
+  constexpr int KST = SD / 16;   // MFMA k-steps per stage
+  int pc[KST];
+#pragma unroll
+  for (int ks = 0; ks < KST; ++ks) pc[ks] = ((2 * ks + h2) ^ kswz(l32)) * 16;
+  const int rowa = (wm * 64 + l32) * RBY;
 
   auto body = [&](auto nbw_c, int col0) {
     constexpr int NBW = decltype(nbw_c)::value;
     // MFMA m of a stage (m = 0 .. NM-1): k-step m / 2NBW, B block (m / 2) % NBW,
     // A block m % 2.  The A pair and B block 0 of a k-step are read for its
     // first MFMA, B block j for MFMA 2j.
-    constexpr int NM = 4 * NBW, PD = 4;
+    constexpr int NM = 2 * KST * NBW, PD = 4;
     static_assert(PD % 2 == 0 && PD <= 2 * NBW, "reads run ahead within one k-step");
-    const int rowb = A_BYTES + (col0 + l32) * 64;
+    const int rowb = A_BYTES + (col0 + l32) * RBY;
     // row-major B: this lane's transposing-read address within a stage for
     // column block j: k row 8 h2 + (lane & 15) / 4, column col0 + 32 j +
     // 16 ((lane >> 4) & 1) + 4 (lane & 3), its 64-byte group swizzled
@@ -1009,7 +1028,7 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
         trb[j] = A_BYTES + (8 * h2 + tr) * 2 * BN + (((col0 >> 5) + j) ^ row_swz(tr)) * 64 +
                  2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     }
-    bf16x8 fa[2][2], fb[2][NBW];
+    bf16x8 fa[KST][2], fb[KST][NBW];
     f32x16 acc[2][NBW];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1020,11 +1039,11 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
       const char *b = sb + pc[ks];
       if (r == 0) {
         fa[ks][0] = *(const bf16x8 *)(b + rowa);
-        fa[ks][1] = *(const bf16x8 *)(b + rowa + 2048);
+        fa[ks][1] = *(const bf16x8 *)(b + rowa + 32 * RBY);
       }
       if (r % 2 == 0) {
         if constexpr (BKM) {
-          fb[ks][r / 2] = *(const bf16x8 *)(b + rowb + (r / 2) * 2048);
+          fb[ks][r / 2] = *(const bf16x8 *)(b + rowb + (r / 2) * 32 * RBY);
         } else {   // k rows 16 ks + 8 h2 + 0..3, then + 4..7, of column block r / 2
           const __bf16 *src = (const __bf16 *)(sb + trb[r / 2] + ks * 16 * 2 * BN);
           const i16x4 lo = ds_read_tr(src), hi4 = ds_read_tr(src + 4 * BN);
@@ -1035,18 +1054,18 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
     auto run = [&](auto whole_c) {
       constexpr bool WHOLE = decltype(whole_c)::value;
 #pragma unroll
-      for (int s = 0; s < DST - 1; ++s)
+      for (int s = 0; s < NS - 1; ++s)
 #pragma unroll
         for (int q = 0; q < LA + LBH; ++q) issue_one(s, q, whole_c);
       wait_landed();
-      if (!WHOLE && DBK > p.K) zero_tail(0);
+      if (!WHOLE && SD > p.K) zero_tail(0);
       wait_lgkmcnt0();
       __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int u = 0; u < PD; ++u) read_at(lds, u);
       for (int kt = 0; kt < nk; ++kt) {
-        const char *cur = lds + (kt & (DST - 1)) * STAGE;
-        const char *nxt = lds + ((kt + 1) & (DST - 1)) * STAGE;   // past the last stage: an unused slot
+        const char *cur = lds + (kt & (NS - 1)) * STAGE;
+        const char *nxt = lds + ((kt + 1) & (NS - 1)) * STAGE;   // past the last stage: an unused slot
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
@@ -1055,14 +1074,14 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
             // kt+1 has landed and all waves are here, its slot may be refilled
             wait_lgkmcnt0();
             wait_landed();
-            if (!WHOLE && kt + 1 < nk && (kt + 1) * DBK + DBK > p.K) zero_tail(kt + 1);
+            if (!WHOLE && kt + 1 < nk && (kt + 1) * SD + SD > p.K) zero_tail(kt + 1);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
           }
           if (m + PD < NM) read_at(cur, m + PD);
           else read_at(nxt, m + PD - NM);
-          // stage kt+3 refills the slot of stage kt-1, released at its barrier
-          if (m < LA + LBH) issue_one(kt + DST - 1, m, whole_c);
+          // stage kt+NS-1 refills the slot of stage kt-1, released at its barrier
+          if (m < LA + LBH) issue_one(kt + NS - 1, m, whole_c);
           const int ks = m / (2 * NBW), j = (m / 2) % NBW, i = m % 2;
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
@@ -1071,7 +1090,7 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
       wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
     };
     if (nk > 0) {
-      if (p.K % DBK == 0) run(std::true_type{});
+      if (p.K % SD == 0) run(std::true_type{});
       else run(std::false_type{});
     }
     gemm_store_tile<2, NBW, false, ACT>(p, acc, m0 + wm * 64, n0 + col0, l32, h2);
@@ -1083,20 +1102,26 @@ __device__ __forceinline__ void gemm_bf16_w8r(const GemmParams &p) {
 #define CHAIN_W8R_KERNEL(NAME, NB0, NB1, ACT, BKM)                                            \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
   void NAME(const GemmParams p) { gemm_bf16_w8r<NB0, NB1, ACT, BKM>(p); }
-#define CHAIN_W8R_KERNELS(SUFFIX, ACT)                                 \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_4_##SUFFIX, 2, 2, ACT, true)   \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_6_##SUFFIX, 3, 3, ACT, true)   \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_8_##SUFFIX, 4, 4, ACT, true)   \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_11_##SUFFIX, 6, 5, ACT, true)  \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_4_##SUFFIX, 2, 2, ACT, false) \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_6_##SUFFIX, 3, 3, ACT, false) \
-  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_8_##SUFFIX, 4, 4, ACT, false) \
+// 64 k per stage (two stages) at 256 columns, and at 352 for k-major B (at 352
+// row-major B would spill); 32 k per stage (four stages) otherwise.
+#define CHAIN_W8R64_KERNEL(NAME, NB0, NB1, ACT, BKM)                                          \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
+  void NAME(const GemmParams p) { gemm_bf16_w8r<NB0, NB1, ACT, BKM, 64>(p); }
+#define CHAIN_W8R_KERNELS(SUFFIX, ACT)                                   \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_4_##SUFFIX, 2, 2, ACT, true)     \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8r_kernel_6_##SUFFIX, 3, 3, ACT, true)     \
+  CHAIN_W8R64_KERNEL(gemm_bf16_w8r_kernel_8_##SUFFIX, 4, 4, ACT, true)   \
+  CHAIN_W8R64_KERNEL(gemm_bf16_w8r_kernel_11_##SUFFIX, 6, 5, ACT, true)  \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_4_##SUFFIX, 2, 2, ACT, false)   \
+  CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_6_##SUFFIX, 3, 3, ACT, false)   \
+  CHAIN_W8R64_KERNEL(gemm_bf16_w8rt_kernel_8_##SUFFIX, 4, 4, ACT, false) \
   CHAIN_W8R_KERNEL(gemm_bf16_w8rt_kernel_11_##SUFFIX, 6, 5, ACT, false)
 CHAIN_W8R_KERNELS(erf, CHAIN_ACT_GELU_ERF)
 CHAIN_W8R_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
 CHAIN_W8R_KERNELS(id, CHAIN_ACT_IDENTITY)
 CHAIN_W8R_KERNELS(silu, CHAIN_ACT_SILU)
 #undef CHAIN_W8R_KERNELS
+#undef CHAIN_W8R64_KERNEL
 #undef CHAIN_W8R_KERNEL
 
 // f32 inputs: 128 x 128 x 32 tiles on v_mfma_f32_32x32x2_f32 (A: lane holds

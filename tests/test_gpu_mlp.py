@@ -141,16 +141,18 @@ def _kmajor(w):
     return w.t().contiguous().t()
 
 
-# On a 256-CU device these shapes select each bf16 tile width (for X.W1, then
-# H.W2): 352 and 352, 256 and 128, 192 and 128, 128 for the small problems.
-# M, N or K is ragged in each.
+# On a 256-CU device these shapes select each bf16 tile width: 256- and
+# 352-wide tiles take 64-deep stages, narrower ones 32-deep.  M, N or K is
+# ragged in each.
 @pytest.mark.parametrize("M,K,N,K2", [
-    (16000, 4096, 1376, 4096),
-    (4000, 1376, 4096, 264),
-    (17900, 72, 1152, 264),     # 192-wide tiles for X.W1, a K tail after two stages
-    (300, 200, 136, 264),
+    (16000, 4096, 1376, 4096),  # 352 and 352 wide; H.W2 with a K tail (1376 = 21 x 64 + 32)
+    (4000, 1376, 4096, 264),    # 256 wide with a K tail, then 128 wide
+    (4000, 4096, 4096, 264),    # 256 wide, whole 64-deep stages, then 128 wide
+    (12000, 4032, 1376, 256),   # 352 wide over 63 whole stages, then 128 wide
+    (17900, 72, 1152, 264),     # 192 wide (uneven loads of B per wave), a K tail after two stages
+    (300, 200, 136, 264),       # 128 wide
     (96, 8, 24, 40),            # K and N below one 32-deep stage: only K-tail stages
-    (16000, 4008, 1376, 264),   # 192-wide tiles (uneven loads of B per wave) with a K tail
+    (16000, 4008, 1376, 264),   # 352 wide with a K tail (4008 = 62 x 64 + 40)
     (33, 40, 8, 16),            # one partial row tile, one 8-column inner block
 ])
 def test_mlp_weight_layouts_agree_and_match_oracle(M, K, N, K2):
