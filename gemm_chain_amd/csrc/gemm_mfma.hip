@@ -598,20 +598,26 @@ CHAIN_DTL_KERNELS(silu, CHAIN_ACT_SILU)
 // sub-blocks, gate then up, each filled by whole 1 KB loads (so every load
 // reads through one descriptor) with 64-byte groups XOR-swizzled by row as in
 // gemm_bf16_w8r, and read with ds_read_b64_tr_b16.
-template <int NBW, bool GATED, int ACT, bool BKM = true>
+template <int NBW, bool GATED, int ACT, bool BKM = true, int SD = DBK>
 __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   constexpr int BN = 64 * NBW, WTN = 32 * NBW;
   constexpr int OBN = GATED ? BN / 2 : BN;   // output columns per tile
   static_assert(!GATED || NBW % 2 == 0, "gated tiles pair 32-row blocks");
-  constexpr int A_BYTES = BM * DBK * 2, B_BYTES = BN * DBK * 2, STAGE = A_BYTES + B_BYTES;
-  constexpr int NLB = BN / 16;                  // 1 KB loads of B per stage
-  constexpr int LA = BM / 16 / 8;               // 1 KB loads of A per wave and stage
+  // SD: k per stage, 32 (a ring of four stages) or 64 (two), as in gemm_bf16_w8r
+  static_assert(SD == 32 || SD == 64, "stage depth");
+  constexpr int NS = SD == 32 ? 4 : 2, KST = SD / 16;
+  constexpr int CPR = SD / 8, RPL = 64 / CPR, RBY = 2 * SD;
+  auto kswz = [](int r) { return SD == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
+  constexpr int A_BYTES = BM * SD * 2, B_BYTES = BN * SD * 2, STAGE = A_BYTES + B_BYTES;
+  static_assert(NS * STAGE <= 160 * 1024, "the ring must fit in LDS");
+  constexpr int NLB = B_BYTES / 1024;           // 1 KB loads of B per stage
+  constexpr int LA = A_BYTES / 1024 / 8;        // 1 KB loads of A per wave and stage
   constexpr int LBH = (NLB + 7) / 8, LBL = NLB / 8;   // of B: waves below NLB % 8 take LBH
   static_assert(BKM || GATED, "row-major B: gated tiles only (a load never spans the two sub-blocks)");
   constexpr int BCH = OBN / 8, BG = OBN / 32;   // row-major sub-block: 16-byte chunks, 64-byte groups per row
-  constexpr int SUB = DBK * OBN * 2;            // bytes of a row-major sub-block
+  constexpr int SUB = SD * OBN * 2;             // bytes of a row-major sub-block
   auto row_swz = [](int r) { return BG % 4 == 0 ? (r & 3) : BG % 4 == 2 ? ((r >> 1) & 1) : 0; };
-  __shared__ __attribute__((aligned(1024))) char lds[DST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
@@ -644,12 +650,13 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
     return (r / WTN) * (WTN / 2) + ((r % WTN) / 32 >> 1) * 32 + r % 32;
   };
   auto bup = [](int r) { return GATED && (((r % WTN) / 32) & 1); };
-  // Lane i of a load fetches row i >> 2 of its 16-row group, logical chunk lc.
-  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  // Lane i of a k-major load fetches row i / CPR of its RPL-row group, logical
+  // chunk lc (the swizzle depends on the group only through the wave's parity).
+  const int lc = (lane % CPR) ^ kswz(RPL * wave + lane / CPR);
   uint32_t aoff[LA], boff[LBH];
 #pragma unroll
   for (int q = 0; q < LA; ++q)
-    aoff[q] = (uint32_t)min(16 * (wave + 8 * q) + (lane >> 2), ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
+    aoff[q] = (uint32_t)min(RPL * (wave + 8 * q) + lane / CPR, ra - 1) * (uint32_t)p.lda * 2u + 16u * lc;
   // Row-major: load L = wave + 8 q fills sub-block L / (NLB / 2) (gate, up);
   // its lane takes chunk g of the sub-block, row brow(q), columns bcolr(q) ..+7
   // (past the tile's last column: its last chunk again).
@@ -661,19 +668,19 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
   };
 #pragma unroll
   for (int q = 0; q < LBH; ++q)
-    boff[q] = BKM ? (uint32_t)min(bcol(16 * (wave + 8 * q) + (lane >> 2)), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc
+    boff[q] = BKM ? (uint32_t)min(bcol(RPL * (wave + 8 * q) + lane / CPR), rb - 1) * (uint32_t)p.b_sn * 2u + 16u * lc
                   : (uint32_t)brow(q) * (uint32_t)p.b_sk * 2u + 2u * (uint32_t)bcolr(q);
   // the descriptor of load q: k-major, by its staged rows; row-major, by its sub-block
-  auto bdesc = [&](int q) { return (BKM ? bup(16 * (wave + 8 * q)) : bsub(q) == 1) ? brs2 : brs; };
-  const int nk = (p.K + DBK - 1) / DBK;
+  auto bdesc = [&](int q) { return (BKM ? bup(RPL * (wave + 8 * q)) : bsub(q) == 1) ? brs2 : brs; };
+  const int nk = (p.K + SD - 1) / SD;
   typedef __attribute__((address_space(3))) void lds_void;
 
-  // Stage kt into ring slot kt % DST; past the last stage, stage 0 again (valid
+  // Stage kt into ring slot kt % NS; past the last stage, stage 0 again (valid
   // data into a slot nobody reads, so every iteration has the same shape).
   auto issue = [&](int kt, auto whole_c) {
-    char *sb = lds + (kt & (DST - 1)) * STAGE;
-    const int k0 = kt < nk ? kt * DBK : 0;
-    if (decltype(whole_c)::value || k0 + DBK <= p.K) {
+    char *sb = lds + (kt & (NS - 1)) * STAGE;
+    const int k0 = kt < nk ? kt * SD : 0;
+    if (decltype(whole_c)::value || k0 + SD <= p.K) {
 #pragma unroll
       for (int q = 0; q < LA; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(sb + (wave + 8 * q) * 1024), 16, aoff[q],
@@ -708,16 +715,16 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
         if (q < LBL || hi)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(bup(16 * (wave + 8 * q)) ? brs2 : brs,
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bup(RPL * (wave + 8 * q)) ? brs2 : brs,
                                                    (lds_void *)(sb + A_BYTES + (wave + 8 * q) * 1024), 16,
                                                    boff[q] + kb, 0, 0, 0);
     }
   };
   // After stage kt (the K tail) has landed: zero the chunks past K.
   auto zero_tail = [&](int kt) {
-    char *sb = lds + (kt & (DST - 1)) * STAGE + lane * 16;
+    char *sb = lds + (kt & (NS - 1)) * STAGE + lane * 16;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    if (kt * DBK + 8 * lc >= p.K) {
+    if (kt * SD + 8 * lc >= p.K) {
 #pragma unroll
       for (int q = 0; q < LA; ++q) *(u32x4 *)(sb + (wave + 8 * q) * 1024) = z;
       if constexpr (BKM) {
@@ -729,23 +736,27 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
     if constexpr (!BKM) {
 #pragma unroll
       for (int q = 0; q < LBH; ++q)
-        if ((q < LBL || hi) && kt * DBK + brow(q) >= p.K) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
+        if ((q < LBL || hi) && kt * SD + brow(q) >= p.K) *(u32x4 *)(sb + A_BYTES + (wave + 8 * q) * 1024) = z;
     }
   };
-  // This wave's loads of stage s have landed (stages s+1 and s+2 may still be
-  // in flight); zero the K tail if stage s holds it.
+  // This wave's loads of stage s have landed (the NS - 2 stages after it may
+  // still be in flight); zero the K tail if stage s holds it.
+  auto wait_landed = [&]() {
+    if (hi) wait_vmcnt<(NS - 2) * (LA + LBH)>();
+    else wait_vmcnt<(NS - 2) * (LA + LBL)>();
+  };
   auto wait_stage = [&](int s) {
-    if (hi) wait_vmcnt<2 * (LA + LBH)>();
-    else wait_vmcnt<2 * (LA + LBL)>();
-    if (s < nk && s * DBK + DBK > p.K) zero_tail(s);
+    wait_landed();
+    if (s < nk && s * SD + SD > p.K) zero_tail(s);
   };
 
   struct Frags {
     bf16x8 a[2], b[NBW];
   };
-  const int sx = (l32 >> 2) & 3;
-  const int pc0 = (h2 ^ sx) * 16, pc1 = ((2 + h2) ^ sx) * 16;
-  const int rowa = (wm * 64 + l32) * 64, rowb = A_BYTES + (wn * WTN + l32) * 64;
+  int pc[KST];
+#pragma unroll
+  for (int ks = 0; ks < KST; ++ks) pc[ks] = ((2 * ks + h2) ^ kswz(l32)) * 16;
+  const int rowa = (wm * 64 + l32) * RBY, rowb = A_BYTES + (wn * WTN + l32) * RBY;
   // row-major: the transposing-read address of block j (gate for even j, up
   // for odd, output column block wn NBW / 2 + j / 2): k row 8 h2 + (lane & 15) / 4
   int trb[NBW];
@@ -757,15 +768,15 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
                2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   }
   auto frags = [&](int kt, int ks, Frags &f) {
-    const char *sb = lds + (kt & (DST - 1)) * STAGE + (ks ? pc1 : pc0);
+    const char *sb = lds + (kt & (NS - 1)) * STAGE + pc[ks];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[i] = *(const bf16x8 *)(sb + rowa + i * 2048);
+    for (int i = 0; i < 2; ++i) f.a[i] = *(const bf16x8 *)(sb + rowa + i * 32 * RBY);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       if constexpr (BKM) {
-        f.b[j] = *(const bf16x8 *)(sb + rowb + j * 2048);
+        f.b[j] = *(const bf16x8 *)(sb + rowb + j * 32 * RBY);
       } else {   // k rows 16 ks + 8 h2 + 0..3, then + 4..7
-        const __bf16 *src = (const __bf16 *)(lds + (kt & (DST - 1)) * STAGE + trb[j] + ks * 16 * 2 * OBN);
+        const __bf16 *src = (const __bf16 *)(lds + (kt & (NS - 1)) * STAGE + trb[j] + ks * 16 * 2 * OBN);
         const i16x4 lo = ds_read_tr(src), hi4 = ds_read_tr(src + 4 * OBN);
         f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       }
@@ -787,13 +798,14 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
 
   constexpr int NM = 2 * NBW;   // MFMAs per k-step
   Frags f0, f1;
-  // The main loop, with the loads of stage kt+3 spread one per MFMA of the first
-  // k-step.  With K a multiple of the stage depth (the usual case) no stage has
-  // a K tail and the loads take the branch-free path.
+  // The main loop, with the loads of stage kt+NS-1 spread one per MFMA of the
+  // first k-step; each k-step's MFMAs run while the next k-step's fragments
+  // are read (f0 and f1 alternate).  With K a multiple of the stage depth (the
+  // usual case) no stage has a K tail and the loads take the branch-free path.
   auto run = [&](auto whole_c) {
     constexpr bool WHOLE = decltype(whole_c)::value;
 #pragma unroll
-    for (int s = 0; s < DST - 1; ++s) issue(s, whole_c);
+    for (int s = 0; s < NS - 1; ++s) issue(s, whole_c);
     wait_stage(0);
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
@@ -801,9 +813,9 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
     for (int kt = 0; kt < nk; ++kt) {
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
-      // stage kt+3 reuses the slot of stage kt-1, whose reads all came before
-      // the previous barrier
-      issue(kt + DST - 1, whole_c);
+      // stage kt+NS-1 reuses the slot of stage kt-1, whose reads all came
+      // before the previous barrier
+      issue(kt + NS - 1, whole_c);
       frags(kt, 1, f1);
       mfmas(f0);
 #pragma unroll
@@ -813,9 +825,26 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (KST == 4) {   // k-steps 1 and 2 (k-step 3 closes the stage below)
+        frags(kt, 2, f0);
+        mfmas(f1);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        frags(kt, 3, f1);
+        mfmas(f0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (WHOLE) {
-        if (hi) wait_vmcnt<2 * (LA + LBH)>();
-        else wait_vmcnt<2 * (LA + LBL)>();
+        wait_landed();
       } else {
         wait_stage(kt + 1);
       }
@@ -834,21 +863,23 @@ __device__ __forceinline__ void gemm_bf16_w8(const GemmParams &p) {
     wait_vmcnt<0>();   // no LDS-bound load may outlive the workgroup
   };
   if (nk > 0) {
-    if (p.K % DBK == 0) run(std::true_type{});
+    if (p.K % SD == 0) run(std::true_type{});
     else run(std::false_type{});
   }
 
   gemm_store_tile<2, NBW, GATED, ACT>(p, acc, m0 + wm * 64, n0 + wn * (GATED ? WTN / 2 : WTN), l32, h2);
 }
 
-#define CHAIN_W8_KERNEL(NAME, NBW, GATED, ACT, BKM)                                           \
+// The 128-output-column gated tiles (256 staged B rows) take 64-deep stages,
+// the 64-column ones 32-deep (too few MFMAs per stage to hide a two-stage ring).
+#define CHAIN_W8_KERNEL(NAME, NBW, GATED, ACT, BKM, SD)                                       \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2))) \
-  void NAME(const GemmParams p) { gemm_bf16_w8<NBW, GATED, ACT, BKM>(p); }
-#define CHAIN_W8_KERNELS(SUFFIX, ACT)                                           \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_2_##SUFFIX, 2, true, ACT, true)     \
-  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_4_##SUFFIX, 4, true, ACT, true)     \
-  CHAIN_W8_KERNEL(gemm_bf16_w8t_gated_kernel_2_##SUFFIX, 2, true, ACT, false)   \
-  CHAIN_W8_KERNEL(gemm_bf16_w8t_gated_kernel_4_##SUFFIX, 4, true, ACT, false)
+  void NAME(const GemmParams p) { gemm_bf16_w8<NBW, GATED, ACT, BKM, SD>(p); }
+#define CHAIN_W8_KERNELS(SUFFIX, ACT)                                             \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_2_##SUFFIX, 2, true, ACT, true, 32)   \
+  CHAIN_W8_KERNEL(gemm_bf16_w8_gated_kernel_4_##SUFFIX, 4, true, ACT, true, 64)   \
+  CHAIN_W8_KERNEL(gemm_bf16_w8t_gated_kernel_2_##SUFFIX, 2, true, ACT, false, 32) \
+  CHAIN_W8_KERNEL(gemm_bf16_w8t_gated_kernel_4_##SUFFIX, 4, true, ACT, false, 64)
 CHAIN_W8_KERNELS(erf, CHAIN_ACT_GELU_ERF)
 CHAIN_W8_KERNELS(tanh, CHAIN_ACT_GELU_TANH)
 CHAIN_W8_KERNELS(id, CHAIN_ACT_IDENTITY)

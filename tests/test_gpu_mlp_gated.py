@@ -104,6 +104,7 @@ def _gated_width(M, N, cus=256):
     (4096, 1376, 4096, 264, 0, 4),   # 128-wide tiles, whole stages
     (4000, 264, 4000, 136, 0, 4),    # 128-wide tiles, ragged N, a K tail after eight stages
     (96, 24, 40, 16, 0, 2),          # K inside one partial stage
+    (4096, 24, 4096, 264, 0, 4),     # 128-wide tiles (64-deep stages) with K inside one partial stage
     (1000, 512, 392, 264, 24, 2),    # gate and up rows padded past N
     (16384, 4096, 1376, 4096, 0, 4),  # the FFN shard
 ])
