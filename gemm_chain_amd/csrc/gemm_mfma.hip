@@ -8,33 +8,29 @@
 // [N, K] weight, as linear layers store it); the MLP runs it twice (act = GeLU
 // into the workspace, then act = identity).
 //
-// bf16: one workgroup per CU computes a 256 x BN tile (BN = 256, 192, 128 or,
-// k-contiguous weights only, 352; picked per launch so the tiles fill whole
-// rounds of the chip with the least padding) on
-// v_mfma_f32_32x32x16_bf16 blocks with f32 accumulators: 4 x 2 waves of
-// 64 x BN/2 (two waves per SIMD) for k-contiguous weights, 2 x 2 waves of
-// 128 x BN/2 (one wave per SIMD, accumulators in AGPRs) otherwise.
-// Operands are swapped in the MFMA (it computes the transposed block) so a lane
-// ends up holding four consecutive output columns of one row: 8-byte stores.
-// Two ways of feeding LDS, by weight layout:
-//  - k-contiguous B: loads that write LDS directly fill a ring of four
-//    k-stages of 32, fetched three stages ahead, rows XOR-swizzled instead of
-//    padded.  gemm_bf16_w8r_kernel_NB runs eight waves (two per SIMD) of 64
-//    rows, the two wave columns taking NB/2 32-column blocks each (6 + 5 for
-//    NB = 11), with buffer loads and streamed fragments;
-//    gemm_bf16_w8_gated_kernel_NBW feeds the gated product the same way;
-//    gemm_bf16_dtl_kernel_NBW, the same ring with four waves of 128 x BN/2,
-//    serves operands whose 256-row tiles span 2 GiB or more (beyond 32-bit
-//    buffer offsets);
-//  - n-contiguous B (gemm_bf16_kernel<NBW>): k-tiles of 64 staged through
-//    registers into two LDS buffers; A as [256][64 + 8], B as [64][BN' + 32]
-//    read with ds_read_b64_tr_b16.
-// Both give the same MFMA operands in the same k order.  The gated MLP's first
-// product (TSP article: gate and up projection shards) runs the k-contiguous
-// kernel with two B matrices whose tiles share the A tile, and multiplies
-// act(gate) by up in the epilogue.  The f32 path for f32
-// inputs keeps a 128 x 128 x 32 tile per 256 threads with
-// v_mfma_f32_32x32x2_f32.
+// bf16: one workgroup per CU computes a 256 x BN tile (BN = 352, 256, 192 or
+// 128, picked per launch so the tiles fill whole rounds of the chip with the
+// least padding) on v_mfma_f32_32x32x16_bf16 blocks with f32 accumulators, as
+// 4 x 2 waves of 64 x BN/2 (two waves per SIMD).  Operands are swapped in the
+// MFMA (it computes the transposed block) so a lane ends up holding four
+// consecutive output columns of one row: 8-byte stores.  Buffer loads that
+// write LDS directly fill a ring of k-stages (four of 32 k, or two of 64 k for
+// the 256- and 352-wide tiles), rows XOR-swizzled instead of padded, and
+// fragments are streamed a few MFMAs ahead of use:
+//  - gemm_bf16_w8r_kernel_NB: k-contiguous B, staged like A (B rows are
+//    output columns), read with 16-byte LDS reads;
+//  - gemm_bf16_w8rt_kernel_NB: n-contiguous B, staged by k row and read with
+//    ds_read_b64_tr_b16 (the transposing read gives the same operand);
+//  - gemm_bf16_w8_gated_kernel_NBW / gemm_bf16_w8t_gated_kernel_NBW: the gated
+//    MLP's first product (TSP article: gate and up projection shards), two B
+//    matrices whose tiles share the A tile, act(gate) times up in the epilogue;
+//  - fallbacks for operands whose tile rows span 2 GiB or more (beyond 32-bit
+//    buffer offsets): gemm_bf16_dtl_kernel_NBW (four waves of 128 x BN/2, the
+//    same ring, k-contiguous B) and gemm_bf16_kernel<NBW> (k-tiles of 64 staged
+//    through registers into two LDS buffers, n-contiguous B).
+// Every path gives the same MFMA operands in the same k order, so the weight
+// layouts and paths give the same bits.  The f32 path for f32 inputs keeps a
+// 128 x 128 x 32 tile per 256 threads with v_mfma_f32_32x32x2_f32.
 #include "internal.h"
 
 #include <type_traits>
