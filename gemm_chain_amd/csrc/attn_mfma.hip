@@ -577,24 +577,48 @@ __device__ __forceinline__ void attn_mfma_bf16(const AttnParams &p) {
       convert_q();
     }
     const float lt = pair_sum(l);
+    // bf16 rows 16-byte aligned: the lane halves swap half of their column
+    // groups (permlane32_swap) so that each lane stores 8 consecutive columns:
+    // half the store instructions, and each writes 32 bytes of a row per lane
+    // pair instead of 16 (the store path's cost goes with the pieces touched)
+    const bool o16 = !p.o_f32 && (uintptr_t)p.o % 16 == 0 && p.o_ss % 8 == 0 && p.o_sh % 8 == 0 && p.o_sb % 8 == 0;
     if (e_ok) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const int64_t orow = b * p.o_sb + head * p.o_sh + (int64_t)e_row * p.o_ss;
+      auto pack2 = [](float x, float y) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 w = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(uint32_t, w);
+      };
+      if (o16) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = db * 32 + 8 * g + 4 * h2;
-          const float o0 = acc[db][4 * g] * inv, o1 = acc[db][4 * g + 1] * inv;
-          const float o2 = acc[db][4 * g + 2] * inv, o3 = acc[db][4 * g + 3] * inv;
-          if (p.o_f32) {
-            *(float4 *)((float *)p.o + orow + d0) = make_float4(o0, o1, o2, o3);
-          } else {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 w = {(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
-            *(bf16x4 *)((__bf16 *)p.o + orow + d0) = w;
+          for (int g = 0; g < 4; g += 2) {
+            const f32x16 &a = acc[db];
+            const auto x0 = __builtin_amdgcn_permlane32_swap(pack2(a[4 * g] * inv, a[4 * g + 1] * inv),
+                                                             pack2(a[4 * g + 4] * inv, a[4 * g + 5] * inv), false, false);
+            const auto x1 = __builtin_amdgcn_permlane32_swap(pack2(a[4 * g + 2] * inv, a[4 * g + 3] * inv),
+                                                             pack2(a[4 * g + 6] * inv, a[4 * g + 7] * inv), false, false);
+            *(u32x4 *)((__bf16 *)p.o + orow + db * 32 + 8 * (g + h2)) = u32x4{x0[0], x1[0], x0[1], x1[1]};
           }
-        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = db * 32 + 8 * g + 4 * h2;
+            const float o0 = acc[db][4 * g] * inv, o1 = acc[db][4 * g + 1] * inv;
+            const float o2 = acc[db][4 * g + 2] * inv, o3 = acc[db][4 * g + 3] * inv;
+            if (p.o_f32) {
+              *(float4 *)((float *)p.o + orow + d0) = make_float4(o0, o1, o2, o3);
+            } else {
+              typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+              bf16x4 w = {(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
+              *(bf16x4 *)((__bf16 *)p.o + orow + d0) = w;
+            }
+          }
+      }
       if (h2 == 0)
         p.lse[b * p.l_sb + head * p.l_sh + (int64_t)e_row * p.l_ss] =
             lt > 0.f ? (m + log2f(lt)) * 0.69314718055994531f : -INFINITY;
