@@ -10,8 +10,7 @@
 // part (coalesced 512-byte row segments per half-wave) with non-temporal
 // loads: the partials are read exactly once.  For the common part counts the
 // count is a template parameter, so all C slices of a lane are requested before
-// the first one is consumed (C x 16 bytes in flight per lane) and each lane
-// works on two rows to double that.  The C LSE values of a row are read by all
+// the first one is consumed (C x 16 bytes in flight per lane).  The C LSE values of a row are read by all
 // 32 lanes at one address (one broadcast transaction).
 #include "internal.h"
 
@@ -27,14 +26,6 @@ struct RowRef {
   int b, h, s;
 };
 
-__device__ inline RowRef row_ref(const MergeParams &p, int64_t row) {
-  RowRef r;
-  r.s = (int)(row % p.S);
-  r.h = (int)((row / p.S) % p.H);
-  r.b = (int)(row / ((int64_t)p.S * p.H));
-  return r;
-}
-
 __device__ inline void store_row(const MergeParams &p, const RowRef &r, int j, f32x4 o) {
   const int64_t orow = r.b * p.o_sb + r.h * p.o_sh + (int64_t)r.s * p.o_ss;
   if (p.o_f32) {
@@ -49,22 +40,31 @@ __device__ inline void store_lse(const MergeParams &p, const RowRef &r, float v)
   if (p.lse) p.lse[r.b * p.l_sb + r.h * p.l_sh + (int64_t)r.s * p.l_ss] = v;
 }
 
-// C known at compile time: two rows per lane group, all loads issued first.
-template <int C>
-__global__ __launch_bounds__(256) void lse_merge_fixed(const MergeParams p) {
-  constexpr int R = 2;  // rows per lane group
+// C known at compile time: all loads of a lane are issued before the first is
+// consumed.  A workgroup covers RPB consecutive rows of one (batch, head): the
+// (b, h) pair and the row block come from the workgroup index by two uniform
+// 32-bit divisions, so no lane divides (64-bit row arithmetic per lane cost the
+// kernel about a tenth of its time).  R rows per lane group: 2 for few parts,
+// so that a lane still has 2 C x 16 bytes in flight; 1 for 8 and more parts,
+// in 512-thread workgroups, which measured a little faster than 2 rows in 256.
+template <int C, int R, int BS>
+__global__ __launch_bounds__(BS) void lse_merge_fixed(const MergeParams p, const uint32_t nsb) {
+  constexpr int RPB = BS / 32 * R;  // rows per workgroup
   const int lr = threadIdx.x & 31;
-  const int64_t rows = (int64_t)p.B * p.H * p.S;
-  const int64_t row0 = ((int64_t)blockIdx.x * kRowsPerPass + (threadIdx.x >> 5)) * R;
+  const uint32_t bh = blockIdx.x / nsb;
+  const int s0 = (int)(blockIdx.x - bh * nsb) * RPB + (int)(threadIdx.x >> 5) * R;
+  const int b = (int)(bh / (uint32_t)p.H), h = (int)bh - b * p.H;
   const int nslices = p.D / 4;
+  const float *lbase = p.lse_parts + b * p.lp_sb + h * p.lp_sh;
+  const float *obase = p.o_parts + b * p.p_sb + h * p.p_sh;
   RowRef ref[R];
   bool live[R];
   float lse[R][C];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    live[i] = row0 + i < rows;
-    ref[i] = row_ref(p, live[i] ? row0 + i : 0);
-    const float *lp = p.lse_parts + ref[i].b * p.lp_sb + ref[i].h * p.lp_sh + (int64_t)ref[i].s * p.lp_ss;
+    live[i] = s0 + i < p.S;
+    ref[i] = {b, h, live[i] ? s0 + i : 0};
+    const float *lp = lbase + (int64_t)ref[i].s * p.lp_ss;
 #pragma unroll
     for (int c = 0; c < C; ++c) lse[i][c] = lp[c * p.lp_sc];
   }
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void lse_merge_fixed(const MergeParams p) {
     f32x4 x[R][C];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const float *op = p.o_parts + ref[i].b * p.p_sb + ref[i].h * p.p_sh + (int64_t)ref[i].s * p.p_ss + 4 * j;
+      const float *op = obase + (int64_t)ref[i].s * p.p_ss + 4 * j;
 #pragma unroll
       for (int c = 0; c < C; ++c) x[i][c] = __builtin_nontemporal_load((const f32x4 *)(op + c * p.p_sc));
     }
@@ -100,15 +100,17 @@ __global__ __launch_bounds__(256) void lse_merge_fixed(const MergeParams p) {
   }
 }
 
-// Any C (up to 64): one row per lane group, parts streamed in order.
-__global__ __launch_bounds__(256) void lse_merge_any(const MergeParams p) {
+// Any C (up to 64): one row per lane group, parts streamed in order; the
+// same per-workgroup (batch, head, row block) decomposition.
+__global__ __launch_bounds__(256) void lse_merge_any(const MergeParams p, const uint32_t nsb) {
   const int lr = threadIdx.x & 31;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerPass + (threadIdx.x >> 5);
-  const int64_t rows = (int64_t)p.B * p.H * p.S;
-  if (row >= rows) return;
-  const RowRef r = row_ref(p, row);
-  const float *lp = p.lse_parts + r.b * p.lp_sb + r.h * p.lp_sh + (int64_t)r.s * p.lp_ss;
-  const float *op = p.o_parts + r.b * p.p_sb + r.h * p.p_sh + (int64_t)r.s * p.p_ss;
+  const uint32_t bh = blockIdx.x / nsb;
+  const int s = (int)(blockIdx.x - bh * nsb) * kRowsPerPass + (int)(threadIdx.x >> 5);
+  if (s >= p.S) return;
+  const int b = (int)(bh / (uint32_t)p.H), h = (int)bh - b * p.H;
+  const RowRef r = {b, h, s};
+  const float *lp = p.lse_parts + b * p.lp_sb + h * p.lp_sh + (int64_t)s * p.lp_ss;
+  const float *op = p.o_parts + b * p.p_sb + h * p.p_sh + (int64_t)s * p.p_ss;
   float M = -INFINITY;
   for (int c = 0; c < p.C; ++c) M = fmaxf(M, lp[c * p.lp_sc]);
   const int nslices = p.D / 4;
@@ -130,11 +132,13 @@ __global__ __launch_bounds__(256) void lse_merge_any(const MergeParams p) {
   if (lr == 0) store_lse(p, r, M == -INFINITY ? -INFINITY : M + logf(wsum));
 }
 
-template <int C>
+template <int C, int R, int BS>
 hipError_t launch_fixed(const MergeParams &p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.H * p.S;
-  const int64_t blocks = (rows + 2 * kRowsPerPass - 1) / (2 * kRowsPerPass);
-  hipLaunchKernelGGL(lse_merge_fixed<C>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  constexpr int RPB = BS / 32 * R;
+  const int64_t nsb = ((int64_t)p.S + RPB - 1) / RPB;
+  const int64_t blocks = nsb * p.B * p.H;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((lse_merge_fixed<C, R, BS>), dim3((unsigned)blocks), dim3(BS), 0, stream, p, (uint32_t)nsb);
   return hipGetLastError();
 }
 
@@ -142,16 +146,17 @@ hipError_t launch_fixed(const MergeParams &p, hipStream_t stream) {
 
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream) {
   switch (p.C) {
-    case 1: return launch_fixed<1>(p, stream);
-    case 2: return launch_fixed<2>(p, stream);
-    case 4: return launch_fixed<4>(p, stream);
-    case 8: return launch_fixed<8>(p, stream);
-    case 16: return launch_fixed<16>(p, stream);
+    case 1: return launch_fixed<1, 2, 256>(p, stream);
+    case 2: return launch_fixed<2, 2, 256>(p, stream);
+    case 4: return launch_fixed<4, 2, 256>(p, stream);
+    case 8: return launch_fixed<8, 1, 512>(p, stream);
+    case 16: return launch_fixed<16, 1, 512>(p, stream);
     default: break;
   }
-  const int64_t rows = (int64_t)p.B * p.H * p.S;
-  const int64_t blocks = (rows + kRowsPerPass - 1) / kRowsPerPass;
-  hipLaunchKernelGGL(lse_merge_any, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  const int64_t nsb = ((int64_t)p.S + kRowsPerPass - 1) / kRowsPerPass;
+  const int64_t blocks = nsb * p.B * p.H;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(lse_merge_any, dim3((unsigned)blocks), dim3(256), 0, stream, p, (uint32_t)nsb);
   return hipGetLastError();
 }
 

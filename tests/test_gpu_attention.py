@@ -294,6 +294,27 @@ def test_merge_part_counts_against_oracle(C, D):
     assert max_abs(f64(mb), ro) <= 2e-2
 
 
+@pytest.mark.parametrize("C", [8, 6])
+def test_merge_strided_parts_match_contiguous(C):
+    """Partials as sequence-major views ([C, B, S, H, D] storage) and their LSE as a slice of a
+    padded buffer: same bits as contiguous parts, across several batches and heads and a
+    ragged last row block."""
+    dev = device()
+    g = torch.Generator().manual_seed(70 + C)
+    B, H, S, D = 3, 5, 45, 128
+    o_sm = torch.randn(C, B, S, H, D, generator=g)
+    l_pad = torch.randn(C, B, H + 2, S + 3, generator=g) * 3
+    l_pad[1, 2, 4, :9] = -math.inf
+    announce(f"merge strided C{C}")
+    o_v, l_v = o_sm.to(dev).permute(0, 1, 3, 2, 4), l_pad.to(dev)[:, :, 1:H + 1, 2:S + 2]
+    mo, ml = chain.lse_merge(o_v, l_v, out_dtype=torch.float32)
+    co, cl = chain.lse_merge(o_v.contiguous(), l_v.contiguous(), out_dtype=torch.float32)
+    assert torch.equal(mo, co) and torch.equal(ml, cl)
+    ro, rl = oracle.lse_merge(o_sm.permute(0, 1, 3, 2, 4).double().numpy(),
+                              l_pad[:, :, 1:H + 1, 2:S + 2].double().numpy())
+    assert max_abs(f64(mo), ro) <= 1e-5 and max_abs(f64(ml), rl) <= 1e-5
+
+
 @pytest.mark.parametrize("D,n_chunks,zigzag", [(128, 5, True), (64, 1, False)])
 def test_strided_kv_views_match_contiguous(D, n_chunks, zigzag):
     """K and V as head-major views ([B, S, H, D] storage): same bits as contiguous inputs."""
