@@ -278,7 +278,12 @@ chain_status chain_lse_merge(const chain_tensor *O_parts, const chain_tensor *LS
     return fail(CHAIN_ERR_ALIAS, "outputs overlap inputs or each other");
   const int64_t rows = O->shape[0] * O->shape[1] * O->shape[2];
   if (rows == 0) return ok();
-  if (rows > (int64_t)INT32_MAX * 8) return fail(CHAIN_ERR_UNSUPPORTED, "too many rows");
+  // the kernels index (batch, head) and row blocks of at least 8 rows by 32-bit
+  // workgroup numbers, and rows by 32-bit positions
+  const int64_t bh = O->shape[0] * O->shape[1], S = O->shape[2];
+  if (S > INT32_MAX || bh > INT32_MAX || bh * ((S + 7) / 8) > INT32_MAX)
+    return fail(CHAIN_ERR_UNSUPPORTED, "too many rows: %lld (batch, head) pairs of %lld rows",
+                (long long)bh, (long long)S);
   chain::MergeParams p;
   std::memset(&p, 0, sizeof p);
   p.o_parts = (const float *)O_parts->data;

@@ -180,7 +180,8 @@ chain_status chain_attn_partial(const chain_tensor *Q, const chain_tensor *Kc,
  *   O         [B, H, S, D]     f32 or bf16 (output, rounded to nearest even)
  *   LSE       [B, H, S]        f32   (output; may be NULL to skip it)
  * Rows whose parts are all -inf give O = 0, LSE = -inf.  1 <= C <= 64.
- * D must be a multiple of 4 and at most 256.
+ * D must be a multiple of 4 and at most 256.  Sizes: S and B*H below 2^31 and
+ * B*H*ceil(S/8) below 2^31, else CHAIN_ERR_UNSUPPORTED.
  */
 chain_status chain_lse_merge(const chain_tensor *O_parts, const chain_tensor *LSE_parts,
                              const chain_tensor *O, const chain_tensor *LSE, void *stream);

@@ -157,6 +157,13 @@ def test_merge_and_mlp_validation_codes(lib):
     assert lib.chain_lse_merge(P(Op), P(Lp7), P(O), P(L), None) == CODES["CHAIN_ERR_SHAPE"]
     Oal = td([1, 4, 256, 64], chain.BF16, FAKE + 64)
     assert lib.chain_lse_merge(P(Op), P(Lp), P(Oal), P(L), None) == CODES["CHAIN_ERR_ALIAS"]
+    # more 8-row blocks of (batch, head) rows than 32-bit workgroup numbers (2^30 + 1 heads of
+    # 9 rows: 9.7e9 rows in 2^31 + 2 blocks), or more heads than 32 bits: refused before any launch
+    for heads, S in [(2 ** 30 + 1, 9), (2 ** 31, 1)]:
+        Oh = td([1, 1, heads, S, 4], chain.F32, FAKE)
+        Lh = td([1, 1, heads, S], chain.F32, FAKE + 2 ** 44)
+        Mo = td([1, heads, S, 4], chain.F32, FAKE + 2 ** 45)
+        assert lib.chain_lse_merge(P(Oh), P(Lh), P(Mo), None, None) == CODES["CHAIN_ERR_UNSUPPORTED"]
 
     X = td([512, 256], chain.BF16, FAKE)
     W1 = td([256, 128], chain.BF16, FAKE + 2 ** 30)
